@@ -1,0 +1,517 @@
+"""Pins of the CPU oracle to facts fixed outside it (no GPU needed).
+
+Each test checks the oracle against something other than itself: hand-worked
+fixtures under ``tests/golden``, closed forms, invariants, exact-rational brute
+force (``tests/_brute.py``), library routines (torch CPU casts, float64
+``rms_norm``) and error bounds. Every part of the oracle is covered by at least
+one pin that a plausible mistake (dropped term, wrong sign or index, swapped
+operand, wrong rounding or tie rule) would break.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from tests import _brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+
+def to_bf16_bits(x):
+    """float array -> bf16 bits via torch's CPU cast (RNE)."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f32(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def ulp_dist_bf16(a, b):
+    """Distance in bf16 steps on the monotone integer line (NaN -> huge)."""
+    def key(u):
+        u = np.asarray(u, dtype=np.int32)
+        return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
+    d = np.abs(key(a) - key(b))
+    nan_a = (np.asarray(a) & 0x7FFF) > 0x7F80
+    nan_b = (np.asarray(b) & 0x7FFF) > 0x7F80
+    d = np.where(nan_a & nan_b, 0, d)
+    return np.where(nan_a ^ nan_b, 1 << 20, d)
+
+
+def _num(tok):
+    tok = tok.strip()
+    if tok == "nan":
+        return float("nan")
+    if "^" in tok:
+        neg = tok.startswith("-")
+        t = tok.lstrip("-")
+        if "*" in t:
+            m, p = t.split("*")
+            v = float(m) * 2.0 ** int(p.split("^")[1])
+        else:
+            v = 2.0 ** int(t.split("^")[1])
+        return -v if neg else v
+    return float(tok)
+
+
+def load_fixture(name):
+    lines = [l.rstrip("\n") for l in open(os.path.join(GOLDEN, name))]
+    lines = [l for l in lines if l.strip() and not l.startswith("#")]
+    fx = {"rows": {}, "slots": {}, "expect": {}, "residual": {}, "cases": [],
+          "x": {}, "scales": {}, "codes": {}, "expect_residual": {}}
+    cur = None
+    for l in lines:
+        head, _, body = l.partition(":")
+        hs = head.split()
+        if hs[0] == "dims":
+            fx["dims"] = {kv.split("=")[0]: int(kv.split("=")[1]) for kv in hs[1:]}
+        elif hs[0] == "row":
+            fx["rows"][(int(hs[1]), int(hs[2]))] = [_num(v) for v in body.split()]
+        elif hs[0] == "slot":
+            r, row, w = body.split()
+            fx["slots"][(int(hs[1]), int(hs[2]))] = (int(r), int(row), float(w))
+        elif hs[0] == "expect":
+            fx["expect"][int(hs[1])] = [_num(v) for v in body.split()]
+        elif hs[0] == "residual":
+            fx["residual"][int(hs[1])] = [_num(v) for v in body.split()]
+        elif hs[0] == "gamma":
+            fx["gamma"] = [_num(v) for v in body.split()]
+        elif hs[0] == "expect_residual":
+            fx["expect_residual"][int(hs[1])] = [_num(v) for v in body.split()]
+        elif hs[0] == "case":
+            cur = {"name": hs[1], "norm": {}}
+            for kv in hs[2:]:
+                k_, v_ = kv.split("=")
+                cur[k_] = float(v_)
+            fx["cases"].append(cur)
+        elif hs[0] == "expect_norm":
+            cur["norm"][int(hs[1])] = [_num(v) for v in body.split()]
+        elif hs[0] == "x":
+            b = body.split()
+            fx["x"][int(hs[1])] = (("negate", int(b[1])) if b[0] == "negate"
+                                   else [_num(v) for v in b])
+        elif hs[0] == "scales":
+            fx["scales"][int(hs[1])] = [int(v) for v in body.split()]
+        elif hs[0] == "codes":
+            fx["codes"][int(hs[1])] = [int(v, 16) for v in body.split()]
+        else:
+            raise ValueError(l)
+    return fx
+
+
+def build_arrays(fx):
+    d = fx["dims"]
+    payload = np.zeros((d["ep"], d["mtpr"], d["H"]), dtype=np.uint16)
+    for (r, row), vals in fx["rows"].items():
+        payload[r, row] = to_bf16_bits(vals)
+    src = np.full((d["T"], d["k"], 2), -1, dtype=np.int32)
+    w = np.zeros((d["T"], d["k"]), dtype=np.float32)
+    for (t, j), (r, row, wj) in fx["slots"].items():
+        src[t, j] = (r, row)
+        w[t, j] = wj
+    return payload, src, w
+
+
+# ------------------------------------------------------- golden fixtures
+
+def test_golden_combine():
+    fx = load_fixture("combine_small.txt")
+    payload, src, w = build_arrays(fx)
+    out = oracle.combine(payload, src, w)
+    for t, vals in fx["expect"].items():
+        np.testing.assert_array_equal(out[t], to_bf16_bits(vals), err_msg=f"token {t}")
+
+
+def test_golden_rmsnorm():
+    fx = load_fixture("rmsnorm_small.txt")
+    payload, src, w = build_arrays(fx)
+    res = np.stack([to_bf16_bits(fx["residual"][t]) for t in sorted(fx["residual"])])
+    gamma = to_bf16_bits(fx["gamma"])
+    assert len(fx["cases"]) == 4
+    for case in fx["cases"]:
+        ro, no = oracle.combine_residual_rmsnorm(
+            payload, src, w, None, res, gamma, case["eps"], case["weight_bias"])
+        for t, vals in fx["expect_residual"].items():
+            np.testing.assert_array_equal(ro[t], to_bf16_bits(vals))
+        for t, vals in case["norm"].items():
+            np.testing.assert_array_equal(no[t], to_bf16_bits(vals),
+                                          err_msg=case["name"])
+
+
+def test_golden_mxfp8():
+    fx = load_fixture("mxfp8_small.txt")
+    d = fx["dims"]
+    x0 = np.array(fx["x"][0], dtype=np.float32)
+    assert fx["x"][1] == ("negate", 0)
+    payload = np.stack([to_bf16_bits(x0), to_bf16_bits(-x0)])[None]
+    # bf16 must hold every hand value exactly, else the fixture is wrong
+    np.testing.assert_array_equal(bf16_to_f32(payload[0, 0]), x0)
+    _, src, w = build_arrays({"dims": d, "rows": {}, "slots": fx["slots"]})
+    codes, scales = oracle.combine_mxfp8(payload, src, w)
+    for t in range(2):
+        assert list(scales[t]) == fx["scales"][t], f"scales token {t}"
+        assert list(codes[t]) == fx["codes"][t], f"codes token {t}"
+
+
+# ------------------------------------------------------ P1: inverse map
+
+@pytest.mark.parametrize("ep,mtpr_pad", [(1, 0), (4, 37), (8, 128)])
+@pytest.mark.parametrize("unit", ["none", "ones"])
+def test_inverse_permutation_bit_exact(ep, mtpr_pad, unit):
+    """top_k = 1 with weight 1: combine(dispatch(x)) returns x exactly
+    (the combine is the inverse of the dispatch scatter)."""
+    rng = np.random.default_rng(11)
+    T, H, E = 97, 64, 16
+    x = to_bf16_bits(rng.standard_normal((T, H)) * 3)
+    topk = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    src, loads = gen.dispatch_slots(topk, np.zeros((T, 1), bool), E, ep, None)
+    mtpr = int(loads.max()) + mtpr_pad
+    payload = gen.scatter_rows(src, x[:, None, :], ep, mtpr,
+                               fill=np.full((ep, mtpr, H), 0x7FC0, np.uint16))
+    w = None if unit == "none" else np.ones((T, 1), np.float32)
+    out = oracle.combine(payload, src, w)
+    np.testing.assert_array_equal(out, x)
+
+
+# --------------------------------------------- P2: identity experts
+
+def test_identity_experts_sum_of_weights():
+    """Every expert returns its input row unchanged: out = bf16(x * sum_j w_j)
+    within one bf16 step (only the fp32 accumulation separates them)."""
+    rng = np.random.default_rng(5)
+    T, H, E, k, ep = 64, 256, 32, 8, 4
+    x = to_bf16_bits(rng.standard_normal((T, H)))
+    inp = gen.make_inputs(dict(T=T, H=H, E=E, ep=ep, k=k), seed=3)
+    payload = gen.scatter_rows(inp.src_info, np.repeat(x[:, None, :], k, axis=1),
+                               ep, inp.mtpr)
+    out = oracle.combine(payload, inp.src_info, inp.weights)
+    ws = inp.weights.astype(np.float64).sum(axis=1)
+    ref = to_bf16_bits(bf16_to_f32(x).astype(np.float64) * ws[:, None])
+    assert ulp_dist_bf16(out, ref).max() <= 1
+
+
+# ------------------------------------------------------------ P3: drops
+
+def test_drop_equals_zero_weight_and_all_dropped():
+    inp = gen.make_inputs(dict(T=40, H=128, E=16, ep=2, k=4, shared_sd=0.5), seed=7)
+    rng = np.random.default_rng(0)
+    mask = rng.random((inp.T, inp.k)) < 0.3
+    src_d = inp.src_info.copy()
+    src_d[mask] = -1
+    w0 = inp.weights.copy()
+    w0[mask] = 0.0
+    for shared in (None, inp.shared):
+        a = oracle.combine(inp.payload, src_d, inp.weights, shared)
+        b = oracle.combine(inp.payload, inp.src_info, w0, shared)
+        np.testing.assert_array_equal(a, b)
+    src_all = np.full_like(inp.src_info, -1)
+    z = oracle.combine(inp.payload, src_all, inp.weights)
+    assert (z == 0).all()                     # +0.0 exactly
+    s = oracle.combine(inp.payload, src_all, inp.weights, inp.shared)
+    np.testing.assert_array_equal(s, inp.shared)
+
+
+# ------------------------------------------------ P4: layout invariance
+
+def test_layout_invariance():
+    """The same (token, slot) rows placed under different ep_size, capacity
+    and row order give bit-identical output: accumulation follows slot order,
+    not payload order."""
+    rng = np.random.default_rng(9)
+    T, H, E, k = 50, 96, 24, 6
+    rows = to_bf16_bits(rng.standard_normal((T, k, H)))
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    outs = []
+    for ep, pad, shuffle in [(1, 0, False), (4, 5, False), (8, 64, True), (2, 1, True)]:
+        src, loads = gen.dispatch_slots(topk, np.zeros((T, k), bool), E, ep, None)
+        mtpr = int(loads.max()) + pad
+        if shuffle:
+            perm = np.stack([rng.permutation(mtpr) for _ in range(ep)])
+            v = src[..., 0] >= 0
+            src[..., 1][v] = perm[src[..., 0][v], src[..., 1][v]]
+        payload = gen.scatter_rows(src, rows, ep, mtpr)
+        outs.append(oracle.combine(payload, src, w))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+# ------------------------------------------------- P5: exact arithmetic
+
+def test_exact_dyadic_sums():
+    """Small integers * 2^-4 with weights in {1/8, ..., 8/8}: every fp32
+    operation is exact, so the output is the exact sum rounded once to bf16."""
+    rng = np.random.default_rng(21)
+    T, H, k, ep, mtpr = 30, 64, 8, 2, 200
+    vals = rng.integers(-16, 17, size=(ep, mtpr, H)) / 16.0
+    payload = to_bf16_bits(vals)
+    assert (bf16_to_f32(payload) == vals).all()
+    src = np.stack([rng.integers(0, ep, (T, k)), rng.integers(0, mtpr, (T, k))],
+                   axis=-1).astype(np.int32)
+    w = (rng.integers(1, 9, size=(T, k)) / 8.0).astype(np.float32)
+    out = oracle.combine(payload, src, w)
+    exact = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            exact[t] += w[t, j] * vals[src[t, j, 0], src[t, j, 1]]
+    np.testing.assert_array_equal(out, to_bf16_bits(exact))
+
+
+# ------------------------------------------ P6: exact-rational brute force
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_routed_sum(seed):
+    """fp32 fused multiply-add chain in exact rationals, one rounding per
+    step, ascending slot order; then bf16 via torch's cast."""
+    inp = gen.make_inputs(dict(T=5, H=16, E=6, ep=2, k=3, shared_sd=2.0,
+                               drop_frac=0.2), seed=seed)
+    pf = bf16_to_f32(inp.payload)
+    sf = bf16_to_f32(inp.shared)
+    ref = np.array(_brute.brute_routed_sum(pf, inp.src_info, inp.weights, sf),
+                   dtype=np.float32)
+    acc = oracle.routed_sum_f32(inp.payload, inp.src_info, inp.weights, inp.shared)
+    np.testing.assert_array_equal(acc.view(np.uint32), ref.view(np.uint32))
+    out = oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared)
+    np.testing.assert_array_equal(out, to_bf16_bits(ref))
+
+
+def test_round_f32_brute_matches_numpy_on_doubles():
+    """The brute-force rounding agrees with the double->float cast."""
+    rng = np.random.default_rng(3)
+    xs = np.concatenate([rng.standard_normal(500) * 10.0 ** rng.integers(-40, 38, 500),
+                         [1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, 2.0 ** -149 * 1.5]])
+    for x in xs:
+        assert _brute.round_f32(Fraction(float(x))) == float(np.float32(x))
+
+
+def test_fp32_accumulation_error_bound():
+    """The fp32 sum is within the recursive-summation bound of the exact sum
+    (k roundings of relative size <= 2^-24 each)."""
+    inp = gen.make_inputs(dict(T=256, H=512, E=64, ep=8, k=8, shared_sd=0.5), seed=4)
+    acc = oracle.routed_sum_f32(inp.payload, inp.src_info, inp.weights, inp.shared)
+    pf = bf16_to_f32(inp.payload).astype(np.float64)
+    exact = np.zeros((inp.T, inp.H))
+    absum = np.zeros((inp.T, inp.H))
+    for j in range(inp.k):
+        r, row = inp.src_info[:, j, 0], inp.src_info[:, j, 1]
+        term = inp.weights[:, j, None].astype(np.float64) * pf[r, row]
+        exact += term
+        absum += np.abs(term)
+    sh = bf16_to_f32(inp.shared).astype(np.float64)
+    exact += sh
+    absum += np.abs(sh)
+    bound = (inp.k + 1) * 2.0 ** -24 * absum * 1.0001
+    assert (np.abs(acc - exact) <= bound).all()
+
+
+# --------------------------------------------- P7: unoccupied rows unread
+
+def test_unoccupied_rows_never_read():
+    c = dict(T=64, H=256, E=32, ep=4, k=4, unoccupied="nan", drop_frac=0.25,
+             shared_sd=0.5, residual_sd=1.0, gamma_sd=0.1)
+    inp = gen.make_inputs(c, seed=2, mtpr=512)
+    assert ((inp.payload & 0x7FFF) > 0x7F80).any()
+    out = oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared)
+    assert not ((out & 0x7FFF) > 0x7F80).any()
+    ro, no = oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
+                                             inp.shared, inp.residual, inp.gamma, 1e-6, 1.0)
+    assert not ((ro & 0x7FFF) > 0x7F80).any() and not ((no & 0x7FFF) > 0x7F80).any()
+    codes, scales = oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights, inp.shared)
+    assert not ((codes & 0x7F) == 0x7F).any() and not (scales == 0xFF).any()
+
+
+def test_checked_mode_rejects_out_of_range_slots():
+    inp = gen.make_inputs("tiny", 0)
+    bad = inp.src_info.copy()
+    bad[3, 1] = (0, inp.mtpr)        # row past capacity
+    with pytest.raises(oracle.OracleError):
+        oracle.combine(inp.payload, bad, inp.weights)
+    bad = inp.src_info.copy()
+    bad[0, 0] = (inp.ep, 0)          # rank past ep_size
+    with pytest.raises(oracle.OracleError):
+        oracle.combine(inp.payload, bad, inp.weights)
+
+
+# ----------------------------------------------------------- P8-P10: RMSNorm
+
+def _rms_inputs(seed=1, T=24, H=512, **kw):
+    c = dict(T=T, H=H, E=32, ep=4, k=8, residual_sd=1.0, gamma_sd=0.1)
+    c.update(kw)
+    return gen.make_inputs(c, seed=seed)
+
+
+def test_rmsnorm_constant_gamma_closed_form():
+    """gamma == c, weight_bias 0: RMS(norm_out) = c * sqrt(ms / (ms + eps))."""
+    inp = _rms_inputs()
+    c, eps = 1.5, 0.25
+    gamma = to_bf16_bits(np.full(inp.H, c))
+    ro, no = oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
+                                             None, inp.residual, gamma, eps, 0.0)
+    x = bf16_to_f32(ro).astype(np.float64)
+    ms = (x * x).mean(axis=1)
+    y = bf16_to_f32(no).astype(np.float64)
+    rms = np.sqrt((y * y).mean(axis=1))
+    np.testing.assert_allclose(rms, c * np.sqrt(ms / (ms + eps)), rtol=2.0 ** -8)
+
+
+def test_rmsnorm_weight_bias_identity():
+    """(gamma == 0, weight_bias 1) is bit-identical to (gamma == 1, wb 0)."""
+    inp = _rms_inputs(seed=2)
+    g0 = to_bf16_bits(np.zeros(inp.H))
+    g1 = to_bf16_bits(np.ones(inp.H))
+    a = oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights, None,
+                                        inp.residual, g0, 1e-6, 1.0)
+    b = oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights, None,
+                                        inp.residual, g1, 1e-6, 0.0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("wb", [0.0, 1.0])
+def test_rmsnorm_matches_torch_float64(wb):
+    """torch.nn.functional.rms_norm in float64 on residual_out, with weight
+    gamma + weight_bias, rounded to bf16, is within one bf16 step; the
+    residual stream equals bf16(fp32 sum + residual) exactly."""
+    inp = _rms_inputs(seed=3, shared_sd=0.5)
+    ro, no = oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
+                                             inp.shared, inp.residual, inp.gamma,
+                                             inp.eps, wb)
+    acc = oracle.routed_sum_f32(inp.payload, inp.src_info, inp.weights, inp.shared)
+    s = torch.from_numpy(acc) + torch.from_numpy(bf16_to_f32(inp.residual))
+    np.testing.assert_array_equal(
+        ro, s.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    x = torch.from_numpy(bf16_to_f32(ro)).double()
+    g = (torch.from_numpy(bf16_to_f32(inp.gamma)) + wb).double()
+    ref = torch.nn.functional.rms_norm(x, (inp.H,), weight=g, eps=inp.eps)
+    refb = ref.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    d = ulp_dist_bf16(no, refb)
+    assert d.max() <= 1
+    # both round double -> fp32 -> bf16, so only summation order separates
+    # them: almost every element is identical. Normalising the unrounded
+    # fp32 sum instead of residual_out would move about a quarter of them.
+    assert (d != 0).mean() <= 1e-3
+
+
+def test_rmsnorm_scale_invariance_eps0():
+    """With eps = 0, scaling payload and residual by 2^j scales residual_out by
+    2^j exactly and leaves norm_out bit-identical."""
+    inp = _rms_inputs(seed=4)
+    base = oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
+                                           None, inp.residual, inp.gamma, 0.0, 0.0)
+    for j in (-5, 3, 11):
+        sc = lambda b: to_bf16_bits(bf16_to_f32(b).astype(np.float64) * 2.0 ** j)
+        ro, no = oracle.combine_residual_rmsnorm(sc(inp.payload), inp.src_info,
+                                                 inp.weights, None, sc(inp.residual),
+                                                 inp.gamma, 0.0, 0.0)
+        np.testing.assert_array_equal(ro, sc(base[0]))
+        np.testing.assert_array_equal(no, base[1])
+
+
+# ------------------------------------------------------------- P11-P14: MXFP8
+
+def test_mx_exponent_closed_form():
+    rng = np.random.default_rng(8)
+    vals = np.concatenate([
+        np.float32(2.0) ** np.arange(-149, 128, dtype=np.float64).astype(np.float32),
+        (rng.random(2000) * 10.0 ** rng.integers(-44, 38, 2000)).astype(np.float32)])
+    for a in vals:
+        a = float(a)
+        if a == 0.0:
+            continue
+        e = _brute.floor_log2(Fraction(a)) - 8
+        assert oracle.mx_exponent(a) == max(-127, min(127, e)), a
+    for n in range(-100, 100):
+        assert oracle.mx_exponent(2.0 ** n) + 127 == max(0, n + 119)
+    assert oracle.mx_exponent(0.0) == -127
+    assert oracle.mx_exponent(float("nan")) + 127 == 0xFF
+    assert oracle.mx_exponent(float("inf")) + 127 == 0xFF
+
+
+def test_e4m3_exhaustive_over_bf16_patterns():
+    """Every bf16 bit pattern (as an fp32 value) against nearest-code search."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    q = (bits << 16).view(np.float32)
+    fin = np.isfinite(q)
+    ref = _brute.nearest_e4m3_vec(q[fin].astype(np.float64))
+    got = np.array([oracle.e4m3_rne_sat(float(v)) for v in q[fin]], dtype=np.uint8)
+    np.testing.assert_array_equal(got, ref)
+    for v in q[~fin]:
+        c = oracle.e4m3_rne_sat(float(v))
+        if np.isnan(v):
+            assert c & 0x7F == 0x7F
+        else:
+            assert c & 0x7F == 0x7E and (c >> 7) == (v < 0)
+
+
+def test_e4m3_random_fp32_and_scalar_brute():
+    rng = np.random.default_rng(12)
+    q = (rng.standard_normal(20000) * 2.0 ** rng.integers(-14, 10, 20000)).astype(np.float32)
+    got = np.array([oracle.e4m3_rne_sat(float(v)) for v in q], dtype=np.uint8)
+    np.testing.assert_array_equal(got, _brute.nearest_e4m3_vec(q.astype(np.float64)))
+    for v in q[:300]:
+        assert oracle.e4m3_rne_sat(float(v)) == _brute.nearest_e4m3(float(v))
+
+
+def test_e4m3_matches_torch_cast_after_clamp():
+    """torch's CPU float8_e4m3fn cast of clamp(q, -448, 448)."""
+    rng = np.random.default_rng(13)
+    q = np.concatenate([(rng.standard_normal(50000) * 2.0 ** rng.integers(-12, 10, 50000)),
+                        np.arange(-520, 520, 0.5)]).astype(np.float32)
+    t = torch.from_numpy(q).clamp(-448, 448).to(torch.float8_e4m3fn)
+    ref = t.view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_rne_sat(float(v)) for v in q], dtype=np.uint8)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_mxfp8_blocks_brute_force_and_bounds():
+    """Tiny shapes: scales and codes from the exact-rational routed sum by
+    search; every block then satisfies the MX invariants and the e4m3 error
+    bound."""
+    inp = gen.make_inputs(dict(T=6, H=64, E=8, ep=2, k=3, hot_row_frac=0.2,
+                               hot_scale=64.0), seed=5)
+    pf = bf16_to_f32(inp.payload)
+    acc = np.array(_brute.brute_routed_sum(pf, inp.src_info, inp.weights), np.float64)
+    codes, scales = oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights)
+    for t in range(inp.T):
+        for b in range(inp.H // 32):
+            blk = acc[t, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            e = -127 if amax == 0 else max(-127, _brute.floor_log2(Fraction(amax)) - 8)
+            assert scales[t, b] == e + 127
+            for i, v in enumerate(blk):
+                q = v * 2.0 ** -e
+                c = int(codes[t, 32 * b + i])
+                assert c == _brute.nearest_e4m3(q)
+                dec = _brute.e4m3_decode(c)
+                if abs(q) < 448:
+                    E = max(_brute.floor_log2(Fraction(abs(q))) if q else -6, -6)
+                    assert abs(dec - q) <= 0.5 * 2.0 ** (E - 3)
+                else:
+                    assert abs(dec) == 448.0
+            if amax > 0 and e > -127:
+                assert 256 <= amax * 2.0 ** -e < 512
+
+
+def test_mxfp8_full_pipeline_consistency():
+    """Codes and scales equal the scalar conversions applied to the oracle's
+    own fp32 sums (links the fused path to the pinned scalar functions), on a
+    generated workload with hot rows, drops and a shared expert."""
+    inp = gen.make_inputs(dict(T=48, H=256, E=32, ep=4, k=8, hot_row_frac=0.05,
+                               drop_frac=0.1, shared_sd=0.5), seed=6)
+    codes, scales = oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights, inp.shared)
+    acc = oracle.routed_sum_f32(inp.payload, inp.src_info, inp.weights, inp.shared)
+    blocks = acc.reshape(inp.T, -1, 32)
+    amax = np.abs(blocks).max(axis=2)
+    e = np.vectorize(oracle.mx_exponent)(amax)
+    np.testing.assert_array_equal(scales, (e + 127).astype(np.uint8))
+    q = blocks * np.exp2(-e.astype(np.float64))[..., None]
+    ref = _brute.nearest_e4m3_vec(q.reshape(-1)).reshape(inp.T, inp.H)
+    np.testing.assert_array_equal(codes, ref)
