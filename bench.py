@@ -1,0 +1,204 @@
+"""Benchmark of the MoE expert combine on one MI355X.
+
+A step is one combine over one batch of synthetic inputs already resident in
+HBM. Several identical copies of the inputs and outputs are rotated from step
+to step, so no launch finds its payload in the 256 MB Infinity Cache or L2
+left by the previous one. Every launch in the timed region is bracketed by
+HIP events on the stream it runs on; their mean is the kernel duration used
+for the roofline. ``value`` is tokens per second of wall-clock time over the
+timed region.
+
+Default workload: T=4096, hidden=7168, top_k=8, 256 experts over 8 simulated
+ranks, bf16 output. Other workloads: --workload skewed | rmsnorm | mxfp8 |
+tiny.
+
+The CPU baseline is the oracle (C, OpenMP), timed on the host cores on the
+same host arrays, repeated for about ten seconds.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "combined tokens/s + achieved HBM GB/s (% peak), T=4096 H=7168 top_k=8"
+PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
+
+KIND = {"dsv3": "bf16", "skewed": "bf16", "tiny": "bf16", "rmsnorm": "rmsnorm",
+        "mxfp8": "mxfp8"}
+DESCR = {
+    "dsv3": "moe combine T=4096 H=7168 top_k=8 E=256 ep=8, bf16 out",
+    "skewed": "moe combine T=8192 H=4096 top_k=8 E=128 ep=8 zipf1.2, 10% drops + capacity, shared expert, bf16 out",
+    "rmsnorm": "moe combine + residual + RMSNorm T=2048 H=7168 top_k=8 E=256 ep=8, weight_bias=1",
+    "mxfp8": "moe combine T=16384 H=7168 top_k=8 E=256 ep=8, MXFP8 e4m3 out + UE8M0/32 scales",
+    "tiny": "moe combine T=64 H=1024 top_k=2 E=8 ep=1, bf16 out",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3", choices=sorted(KIND))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input copies rotated per step (0: enough for >= 1.5 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the kernel")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the combine has no multi-GPU path here).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import moe_expert_combine_amd as mc
+
+    kind = KIND[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
+    inp = gen.make_inputs(args.workload, args.seed)
+    T, H, k, ep, mtpr = inp.T, inp.H, inp.k, inp.ep, inp.mtpr
+    algo_bytes = gen.algorithmic_bytes(inp, kind)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = dict(payload=d16(inp.payload), src=torch.from_numpy(inp.src_info).to(dev),
+                w=torch.from_numpy(inp.weights).to(dev),
+                shared=None if inp.shared is None else d16(inp.shared))
+    if kind == "rmsnorm":
+        base["res"] = d16(inp.residual)
+        base["gamma"] = d16(inp.gamma)
+    per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    nsets = args.sets or min(16, max(1, -(-int(1.5 * 2 ** 30) // max(per_set, 1))))
+    sets = []
+    for i in range(nsets):
+        s = {kk: (None if v is None else (v if i == 0 else v.clone())) for kk, v in base.items()}
+        if kind == "bf16":
+            s["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        elif kind == "rmsnorm":
+            s["ro"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            s["no"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        else:
+            s["codes"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
+            s["scales"] = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    L = mc.lib()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    P = lambda t: None if t is None else t.data_ptr()
+    calls = []
+    for s in sets:
+        if kind == "bf16":
+            a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["out"]),
+                 T, H, k, ep, mtpr, sptr)
+            calls.append((L.moe_combine, a))
+        elif kind == "rmsnorm":
+            a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["res"]),
+                 P(s["gamma"]), inp.eps, 1.0, P(s["ro"]), P(s["no"]), T, H, k, ep, mtpr, sptr)
+            calls.append((L.moe_combine_residual_rmsnorm, a))
+        else:
+            a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["codes"]),
+                 P(s["scales"]), T, H, k, ep, mtpr, sptr)
+            calls.append((L.moe_combine_mxfp8, a))
+
+    def step(i):
+        fn, a = calls[i % len(calls)]
+        st = fn(*a)
+        if st != 0:
+            raise RuntimeError(L.moe_combine_last_error().decode())
+
+    print(f"[bench] warmup {args.warmup} steps ({nsets} input sets)", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    kernel_ms = float(kms.mean())
+    ms_per_step = wall * 1e3 / K
+    tokens_per_s = T * K / wall
+    achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
+    print(f"[bench] kernel mean {kernel_ms * 1e3:.1f} us (p10 {np.percentile(kms, 10) * 1e3:.1f}, "
+          f"p90 {np.percentile(kms, 90) * 1e3:.1f}), {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("workload") == args.workload:
+            traffic = tr.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        if kind == "bf16":
+            run = lambda: oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared, checked=False)
+        elif kind == "rmsnorm":
+            run = lambda: oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
+                                                          inp.shared, inp.residual, inp.gamma,
+                                                          inp.eps, 1.0, checked=False)
+        else:
+            run = lambda: oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights, inp.shared,
+                                               checked=False)
+        run()
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds:
+            c0 = time.perf_counter()
+            run()
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        cpu = {"value": T * reps / t_cpu, "unit": "tokens/s", "cores": oracle.max_threads(),
+               "kind": "oracle",
+               "sample": f"whole workload ({T} tokens) repeated {reps} times, {t_cpu:.1f} s"}
+
+    rec = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": DESCR[args.workload], "num_tokens": T, "hidden": H,
+                   "top_k": k, "ep_size": ep, "max_tokens_per_rank": mtpr,
+                   "kept_slots": inp.meta["kept_slots"], "io_dtype": "bf16",
+                   "seed": args.seed, "input_sets": nsets,
+                   "launch": mc.describe_launch({"bf16": 0, "rmsnorm": 1, "mxfp8": 2}[kind], T, H, k)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": algo_bytes,
+                     "kernel_us_mean": kernel_ms * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * moe_combine.h -- C ABI of the MI355X (gfx950) MoE expert-combine library.
+ *
+ * The combine returns each token's routed expert outputs to it and reduces
+ * them. For token t, hidden index h, and slots j = 0..top_k-1 in ascending
+ * order:
+ *
+ *   (rank, row) = src_info[t, j]              -- rank < 0: dropped slot
+ *   acc  = +0.0f
+ *   acc  = fmaf(w[t, j], payload[rank, row, h], acc)   for every kept slot
+ *   acc += shared_out[t, h]                   -- only if shared_out != NULL
+ *
+ * The sum is accumulated in fp32 in that fixed order. It is followed by one
+ * of three epilogues: a bf16 store (moe_combine), residual add plus RMSNorm
+ * (moe_combine_residual_rmsnorm), or MXFP8 quantisation
+ * (moe_combine_mxfp8).
+ *
+ * Sources (documentation pages):
+ *  - flashinfer.comm.moe_a2a_combine, Parameters: payload, output_dtype,
+ *    output_scales, sf_layout, output; and Returns.
+ *  - Struct_ep_combine_skip_a2a, execute: the summary, the Parameters
+ *    fused_shared_expert and has_epilogue_fusion, and the Args
+ *    output_tokens, src_info, router_weights and topk_ids.
+ *  - flashinfer.megamoe.nvfp4_mega_moe, Parameters: y and num_tokens
+ *    ("-1" rows contribute nothing); and Notes (contiguous tensors on one
+ *    device).
+ *  - flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters: residual_in,
+ *    rms_gamma, rms_eps, residual_out, norm_out and weight_bias.
+ *
+ * Conventions common to every entry point:
+ *  - Pointers are device pointers to caller-owned, contiguous, row-major
+ *    memory on the current HIP device. The library allocates nothing, keeps
+ *    no state between calls, and never synchronises. Work is enqueued on
+ *    `stream`, a hipStream_t; NULL means the default stream. Inputs must be
+ *    unchanged, and outputs untouched, until that work completes.
+ *  - bf16 tensors use 16-bit bfloat16 elements.
+ *  - payload: [ep_size, max_tokens_per_rank, hidden] bf16. Per-expert-rank
+ *    output rows are in dispatch order.
+ *  - src_info: [num_tokens, top_k, 2] int32 = (rank, row) per (token, slot).
+ *    A slot with rank < 0 is dropped: it reads nothing, and its weight is
+ *    ignored (the other weights are not renormalised). For a kept slot the
+ *    caller guarantees 0 <= rank < ep_size and 0 <= row <
+ *    max_tokens_per_rank. The library does not check slot ranges on the
+ *    device; an out-of-range slot reads outside the payload.
+ *  - router_weights: [num_tokens, top_k] fp32, or NULL for unit weights.
+ *  - shared_out: [num_tokens, hidden] bf16, or NULL. It is added unweighted,
+ *    after the routed sum.
+ *  - Outputs have at least num_tokens rows. Exactly the first num_tokens
+ *    rows are written; rows past them are untouched. Outputs must not
+ *    overlap any input, except where an entry point allows it.
+ *  - hidden must be a positive multiple of 8 (16-byte rows). bf16 pointers
+ *    must be 16-byte aligned, src_info 8-byte aligned, router_weights 4-byte
+ *    aligned. 1 <= top_k <= 32, ep_size >= 1, max_tokens_per_rank >= 1, and
+ *    num_tokens >= 0. num_tokens == 0 returns MOE_OK and launches nothing.
+ *  - Rounding: every float -> bf16 conversion rounds to nearest, ties to even.
+ *  - Errors: argument errors return MOE_ERR_INVALID_ARG before any HIP call.
+ *    A failed launch returns MOE_ERR_HIP. moe_combine_last_error() describes
+ *    the last failure on the calling thread.
+ */
+#ifndef MOE_COMBINE_H_
+#define MOE_COMBINE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_HIP = 3
+} moe_status_t;
+
+#define MOE_COMBINE_ABI_VERSION 1
+
+/* Version of this ABI (MOE_COMBINE_ABI_VERSION). */
+int moe_combine_abi_version(void);
+
+/* Static name of a status code. */
+const char *moe_combine_status_string(int status);
+
+/* Message for the last failing call on the calling thread. The string is
+ * owned by the library and valid until this thread's next call. */
+const char *moe_combine_last_error(void);
+
+/*
+ * Routed combine with a bf16 output.
+ *   out[t, h] = bf16(acc)       out: [>= num_tokens, hidden] bf16
+ * Sources: flashinfer.comm.moe_a2a_combine (summary; Parameters payload,
+ * output_dtype = bf16, output), and Struct_ep_combine_skip_a2a, execute
+ * (summary; Args output_tokens, src_info, router_weights; Parameter
+ * fused_shared_expert).
+ */
+moe_status_t moe_combine(const void *payload, const int32_t *src_info,
+                         const float *router_weights, const void *shared_out,
+                         void *out, int64_t num_tokens, int32_t hidden,
+                         int32_t top_k, int32_t ep_size,
+                         int64_t max_tokens_per_rank, void *stream);
+
+/*
+ * Routed combine fused with a residual add and an RMSNorm.
+ *   s                = acc + residual_in[t, h]                      (fp32)
+ *   residual_out     = bf16(s)
+ *   rstd             = 1 / sqrt(mean_h(residual_out^2) + eps)
+ *   norm_out[t, h]   = bf16(residual_out * rstd * (gamma[h] + weight_bias))
+ * weight_bias = 0 gives the standard RMSNorm; 1 gives the (1 + gamma) form.
+ * residual_in, residual_out and norm_out are [>= num_tokens, hidden] bf16;
+ * gamma is [hidden] bf16. residual_out may equal residual_in (in-place
+ * update). norm_out must differ from both of them.
+ * Source: flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters
+ * residual_in, rms_gamma, rms_eps, residual_out, norm_out, weight_bias.
+ */
+moe_status_t moe_combine_residual_rmsnorm(
+    const void *payload, const int32_t *src_info, const float *router_weights,
+    const void *shared_out, const void *residual_in, const void *gamma,
+    float eps, float weight_bias, void *residual_out, void *norm_out,
+    int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t ep_size,
+    int64_t max_tokens_per_rank, void *stream);
+
+/*
+ * Routed combine with an MXFP8 output: float8 e4m3fn codes plus one UE8M0
+ * scale byte per 32 consecutive elements of a row.
+ *
+ * For each block of 32 sums, amax is their largest magnitude. Then:
+ *   e     = clamp(floor(log2(amax)) - 8, -127, 127), with e = -127 if amax == 0
+ *   scale = e + 127                       (0xFF if the block holds NaN or inf)
+ *   code  = e4m3(acc * 2^-e), rounded to nearest even and saturated to +-448
+ *
+ * A NaN or inf block has its codes taken with e = 0: NaN encodes as 0x7F or
+ * 0xFF, and inf saturates. Here 8 is the exponent of e4m3's largest finite
+ * value, 448 = 1.75 * 2^8.
+ *
+ * out_fp8 is [>= num_tokens, hidden] e4m3fn (8-byte aligned). out_scales is
+ * [>= num_tokens, hidden / 32] uint8, linear row-major. hidden must be a
+ * multiple of 32.
+ *
+ * Source: flashinfer.comm.moe_a2a_combine, Parameters output_dtype
+ * (float8_e4m3fn), output_scales (UE8M0, vector size 32) and sf_layout
+ * (linear).
+ */
+moe_status_t moe_combine_mxfp8(const void *payload, const int32_t *src_info,
+                               const float *router_weights,
+                               const void *shared_out, void *out_fp8,
+                               uint8_t *out_scales, int64_t num_tokens,
+                               int32_t hidden, int32_t top_k, int32_t ep_size,
+                               int64_t max_tokens_per_rank, void *stream);
+
+/*
+ * Describes the launch an entry point would make for these sizes, without
+ * touching the GPU. kind: 0 = moe_combine, 1 = residual + RMSNorm,
+ * 2 = MXFP8.
+ *
+ * On success, writes a NUL-terminated text into buf, such as
+ * "threads=128 vec_per_thread=1 chunks=7 blocks=28672 slot_tile=8 masked=0",
+ * and returns MOE_OK. It validates the sizes like the entry point does.
+ * The environment variable MOE_COMBINE_TILE="<threads>x<vectors>"
+ * overrides the threads per block and the 16-byte vectors per thread of
+ * every entry point.
+ */
+moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens,
+                                         int32_t hidden, int32_t top_k,
+                                         char *buf, int32_t buflen);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_COMBINE_H_ */

@@ -1,0 +1,200 @@
+"""MI355X-native MoE expert combine: thin Python binding of the C ABI.
+
+Every function here only checks and marshals arguments (dtype, shape, device,
+contiguity) and calls the entry point of the same name in
+``libmoe_combine.so`` (hand-written HIP kernels for gfx950, declared in
+``include/moe_combine.h``) on torch's current HIP stream. All arithmetic runs
+in those kernels. There is no fallback: if the library cannot be loaded,
+every call raises.
+
+Layouts (see the header for the full contract):
+  payload        bf16  [ep_size, max_tokens_per_rank, hidden]
+  src_info       int32 [num_tokens, top_k, 2]   (rank, row); rank < 0 dropped
+  router_weights fp32  [num_tokens, top_k]      or None (unit weights)
+  shared_out     bf16  [num_tokens, hidden]     or None
+Outputs may be passed in with at least num_tokens rows; only the first
+num_tokens rows are written.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+__all__ = ["moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
+           "describe_launch", "abi_version", "lib", "library_path",
+           "MoeCombineError"]
+
+library_path = _build.LIB
+
+
+class MoeCombineError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, fn, status, msg):
+        self.status = status
+        super().__init__(f"{fn}: {_status_name(status)}: {msg}")
+
+
+_lib = None
+
+
+def _load():
+    """Load the library; build it first only if no build exists."""
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    dims = [I64, I32, I32, I32, I64, P]
+    L.moe_combine.argtypes = [P, P, P, P, P] + dims
+    L.moe_combine_residual_rmsnorm.argtypes = [P, P, P, P, P, P, F, F, P, P] + dims
+    L.moe_combine_mxfp8.argtypes = [P, P, P, P, P, P] + dims
+    for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8"):
+        getattr(L, f).restype = ctypes.c_int
+    L.moe_combine_describe_launch.argtypes = [ctypes.c_int, I64, I32, I32, ctypes.c_char_p, I32]
+    L.moe_combine_describe_launch.restype = ctypes.c_int
+    L.moe_combine_abi_version.argtypes = []
+    L.moe_combine_abi_version.restype = ctypes.c_int
+    L.moe_combine_status_string.argtypes = [ctypes.c_int]
+    L.moe_combine_status_string.restype = ctypes.c_char_p
+    L.moe_combine_last_error.argtypes = []
+    L.moe_combine_last_error.restype = ctypes.c_char_p
+    return L
+
+
+def lib():
+    """The loaded ctypes library (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def _status_name(st):
+    return lib().moe_combine_status_string(st).decode()
+
+
+def _check(fn, st):
+    if st != 0:
+        raise MoeCombineError(fn, st, lib().moe_combine_last_error().decode())
+
+
+def abi_version() -> int:
+    return lib().moe_combine_abi_version()
+
+
+def describe_launch(kind: int, num_tokens: int, hidden: int, top_k: int) -> str:
+    """Launch shape an entry point would use (kind 0 bf16, 1 RMSNorm, 2 MXFP8)."""
+    buf = ctypes.create_string_buffer(256)
+    _check("moe_combine_describe_launch",
+           lib().moe_combine_describe_launch(kind, num_tokens, hidden, top_k, buf, 256))
+    return buf.value.decode()
+
+
+# ----------------------------------------------------------------- checks
+
+def _need(t, name, dtype, device, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+
+
+def _common(payload, src_info, router_weights, shared_out):
+    if not isinstance(payload, torch.Tensor) or payload.device.type != "cuda":
+        raise ValueError("payload must be a GPU tensor")
+    dev = payload.device
+    _need(payload, "payload", torch.bfloat16, dev, 3)
+    _need(src_info, "src_info", torch.int32, dev, 3)
+    if src_info.shape[2] != 2:
+        raise ValueError("src_info must be [num_tokens, top_k, 2]")
+    ep, mtpr, H = payload.shape
+    T, k, _ = src_info.shape
+    if router_weights is not None:
+        _need(router_weights, "router_weights", torch.float32, dev, 2)
+        if tuple(router_weights.shape) != (T, k):
+            raise ValueError(f"router_weights must be [{T}, {k}]")
+    if shared_out is not None:
+        _need(shared_out, "shared_out", torch.bfloat16, dev, 2)
+        if tuple(shared_out.shape) != (T, H):
+            raise ValueError(f"shared_out must be [{T}, {H}]")
+    return dev, (T, H, k, ep, mtpr)
+
+
+def _out(t, name, dtype, dev, T, cols, make):
+    if t is None:
+        return make()
+    _need(t, name, dtype, dev, 2)
+    if t.shape[0] < T or t.shape[1] != cols:
+        raise ValueError(f"{name} must be [>= {T}, {cols}] (got {tuple(t.shape)})")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+# ------------------------------------------------------------ entry points
+
+def moe_combine(payload, src_info, router_weights=None, shared_out=None, out=None):
+    """bf16 combine; returns ``out`` ([num_tokens, hidden] bf16 if None)."""
+    dev, (T, H, k, ep, mtpr) = _common(payload, src_info, router_weights, shared_out)
+    out = _out(out, "out", torch.bfloat16, dev, T, H,
+               lambda: torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+    _check("moe_combine", lib().moe_combine(
+        _ptr(payload), _ptr(src_info), _ptr(router_weights), _ptr(shared_out), _ptr(out),
+        T, H, k, ep, mtpr, _stream(dev)))
+    return out
+
+
+def moe_combine_residual_rmsnorm(payload, src_info, router_weights, shared_out,
+                                 residual_in, gamma, eps, weight_bias=0.0,
+                                 residual_out=None, norm_out=None):
+    """Combine + residual add + RMSNorm; returns (residual_out, norm_out).
+    ``weight_bias`` None means 0.0; ``residual_out`` may be ``residual_in``."""
+    dev, (T, H, k, ep, mtpr) = _common(payload, src_info, router_weights, shared_out)
+    _need(residual_in, "residual_in", torch.bfloat16, dev, 2)
+    if residual_in.shape[0] < T or residual_in.shape[1] != H:
+        raise ValueError(f"residual_in must be [>= {T}, {H}]")
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    if gamma.shape[0] != H:
+        raise ValueError(f"gamma must be [{H}]")
+    mk = lambda: torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    residual_out = _out(residual_out, "residual_out", torch.bfloat16, dev, T, H, mk)
+    norm_out = _out(norm_out, "norm_out", torch.bfloat16, dev, T, H, mk)
+    wb = 0.0 if weight_bias is None else float(weight_bias)
+    _check("moe_combine_residual_rmsnorm", lib().moe_combine_residual_rmsnorm(
+        _ptr(payload), _ptr(src_info), _ptr(router_weights), _ptr(shared_out),
+        _ptr(residual_in), _ptr(gamma), float(eps), wb, _ptr(residual_out),
+        _ptr(norm_out), T, H, k, ep, mtpr, _stream(dev)))
+    return residual_out, norm_out
+
+
+def moe_combine_mxfp8(payload, src_info, router_weights=None, shared_out=None,
+                      out_fp8=None, out_scales=None):
+    """MXFP8 combine; returns (out_fp8 float8_e4m3fn [T, H], out_scales uint8
+    [T, H/32] UE8M0, linear layout)."""
+    dev, (T, H, k, ep, mtpr) = _common(payload, src_info, router_weights, shared_out)
+    if H % 32:
+        raise ValueError("hidden must be a multiple of 32 for MXFP8")
+    out_fp8 = _out(out_fp8, "out_fp8", torch.float8_e4m3fn, dev, T, H,
+                   lambda: torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev))
+    out_scales = _out(out_scales, "out_scales", torch.uint8, dev, T, H // 32,
+                      lambda: torch.empty((T, H // 32), dtype=torch.uint8, device=dev))
+    _check("moe_combine_mxfp8", lib().moe_combine_mxfp8(
+        _ptr(payload), _ptr(src_info), _ptr(router_weights), _ptr(shared_out),
+        _ptr(out_fp8), _ptr(out_scales), T, H, k, ep, mtpr, _stream(dev)))
+    return out_fp8, out_scales

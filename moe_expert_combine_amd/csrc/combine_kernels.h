@@ -1,0 +1,275 @@
+// Device code of the MoE expert combine for CDNA4 (gfx950).
+//
+// One kernel template covers the three outputs. A workgroup of `blockDim.x`
+// threads owns one (token, chunk) pair; a chunk is `blockDim.x * V`
+// consecutive 16-byte vectors (8 bf16) of the hidden dimension. Thread i
+// holds vectors chunk_base + v * blockDim.x + i, v < V, so every load and
+// store instruction of a wavefront covers 1 KiB of contiguous memory.
+//
+// Per token the slot map and weights are wave-uniform (scalar loads). For
+// each group of KT slots all row loads are issued before any arithmetic, so
+// a lane keeps KT * V 16-byte loads in flight; dropped slots (rank < 0) are
+// skipped with a uniform branch and read nothing.
+//
+// Arithmetic (Struct_ep_combine_skip_a2a, execute: weighted sum of the
+// routed expert outputs; Parameter fused_shared_expert): acc starts at +0 and
+// takes one fp32 fused multiply-add per kept slot in ascending slot order,
+// then the unweighted shared-expert term. No MFMA: the work is a gather and
+// a weighted sum, bound by HBM bandwidth.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+enum Epilogue { EPI_BF16 = 0, EPI_RMSNORM = 1, EPI_MXFP8 = 2 };
+
+struct KernelArgs {
+    const uint16_t *payload;   // [ep, mtpr, H] bf16
+    const int32_t *src_info;   // [T, k, 2]
+    const float *weights;      // [T, k] or null (unit weights)
+    const uint16_t *shared;    // [T, H] or null
+    const uint16_t *residual;  // [T, H]   (RMSNorm)
+    const uint16_t *gamma;     // [H]      (RMSNorm)
+    void *out0;                // bf16 out | residual_out | e4m3 codes
+    void *out1;                // norm_out | UE8M0 scales
+    int64_t mtpr;              // rows per rank
+    int32_t H;                 // hidden
+    int32_t nvec;              // H / 8
+    int32_t k;                 // top_k
+    int32_t chunks;            // workgroups per token
+    float eps;
+    float wb;
+};
+
+// bf16 element e (0..7) of a 16-byte vector, widened exactly to fp32.
+__device__ __forceinline__ float bf16_elem(const u32x4 &x, int e) {
+    const unsigned w = x[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+// Two fp32 -> packed bf16 pair (low half = a), round to nearest even; on
+// gfx950 this is the hardware v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(unsigned, r);
+}
+
+// fp32 magnitude bits -> float8 e4m3fn code magnitude (0..0x7F): round to
+// nearest even on the e4m3 grid, saturate at 448, NaN -> 0x7F. Integer route:
+// for normal e4m3 values the fp32 pattern is rounded to 3 mantissa bits and
+// rebiased (fp32 bias 127 -> e4m3 bias 7); below 2^-6 the value is scaled by
+// 2^9 (exact) and rounded to an integer number of subnormal steps.
+__device__ __forceinline__ unsigned e4m3_mag(unsigned a) {
+    if (a > 0x7F800000u) return 0x7Fu;               // NaN
+    if (a >= 0x43E00000u) return 0x7Eu;              // >= 448 (and inf)
+    if (a >= 0x3C800000u) {                          // >= 2^-6
+        const unsigned r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        return (r >> 20) - (120u << 3);
+    }
+    return (unsigned)__builtin_rintf(__uint_as_float(a) * 512.0f);
+}
+
+// Max over the 4 lanes of a DPP quad (lanes 4m..4m+3).
+__device__ __forceinline__ int quad_max(int v) {
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+    return v;
+}
+
+// Sum over the workgroup; every thread gets the same value (fixed order).
+__device__ __forceinline__ float block_sum(float v, float *lds) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wid] = v;
+    __syncthreads();
+    const int nw = (blockDim.x + 63) >> 6;
+    float s = 0.0f;
+    for (int i = 0; i < nw; ++i) s += lds[i];
+    return s;
+}
+
+template <int KT, int V, int EPI, bool MASK>
+__global__ __launch_bounds__(1024) void combine_kernel(KernelArgs a) {
+    __shared__ float lds_red[16];
+    const int nt = blockDim.x;
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x / a.chunks;
+    const int c = blockIdx.x - t * a.chunks;
+    const int64_t row_off = (int64_t)t * a.H;          // output/shared row
+
+    int vi[V];
+    bool ok[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        vi[v] = (c * V + v) * nt + tid;
+        ok[v] = !MASK || vi[v] < a.nvec;
+    }
+
+    float acc[V][8];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
+
+    const int32_t *__restrict__ si = a.src_info + (int64_t)t * a.k * 2;
+    const float *__restrict__ wt = a.weights ? a.weights + (int64_t)t * a.k : nullptr;
+
+    for (int g = 0; g < a.k; g += KT) {
+        const uint16_t *base[KT];
+        bool valid[KT];
+        float w[KT];
+        int r[KT], row[KT];
+        if (g + KT <= a.k) {
+            // full group: straight-line loads that merge into wide scalar loads
+#pragma unroll
+            for (int jj = 0; jj < KT; ++jj) {
+                r[jj] = si[2 * (g + jj)];
+                row[jj] = si[2 * (g + jj) + 1];
+            }
+            if (wt) {
+#pragma unroll
+                for (int jj = 0; jj < KT; ++jj) w[jj] = wt[g + jj];
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < KT; ++jj) w[jj] = 1.0f;
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < KT; ++jj) {
+                const int j = g + jj;
+                const bool in = j < a.k;
+                r[jj] = in ? si[2 * j] : -1;
+                row[jj] = in ? si[2 * j + 1] : 0;
+                w[jj] = (in && wt) ? wt[j] : 1.0f;
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < KT; ++jj) {
+            valid[jj] = r[jj] >= 0;
+            base[jj] = valid[jj] ? a.payload + ((int64_t)r[jj] * a.mtpr + row[jj]) * a.H : a.payload;
+        }
+        u32x4 x[KT][V];
+#pragma unroll
+        for (int jj = 0; jj < KT; ++jj) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                x[jj][v] = (u32x4){0u, 0u, 0u, 0u};
+                if (valid[jj] && ok[v])
+                    x[jj][v] = *reinterpret_cast<const u32x4 *>(base[jj] + (int64_t)vi[v] * 8);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < KT; ++jj) {
+            if (!valid[jj]) continue;
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[v][e] = __builtin_fmaf(w[jj], bf16_elem(x[jj][v], e), acc[v][e]);
+        }
+    }
+
+    if (a.shared) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (!ok[v]) continue;
+            const u32x4 s = *reinterpret_cast<const u32x4 *>(a.shared + row_off + (int64_t)vi[v] * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[v][e] = acc[v][e] + bf16_elem(s, e);
+        }
+    }
+
+    if constexpr (EPI == EPI_BF16) {
+        uint16_t *out = static_cast<uint16_t *>(a.out0);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (!ok[v]) continue;
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[v][2 * i], acc[v][2 * i + 1]);
+            *reinterpret_cast<u32x4 *>(out + row_off + (int64_t)vi[v] * 8) = o;
+        }
+    } else if constexpr (EPI == EPI_RMSNORM) {
+        // flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters residual_in,
+        // residual_out, rms_gamma, rms_eps, norm_out, weight_bias.
+        uint16_t *res_out = static_cast<uint16_t *>(a.out0);
+        uint16_t *norm_out = static_cast<uint16_t *>(a.out1);
+        float ss = 0.0f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (!ok[v]) continue;
+            const u32x4 r = *reinterpret_cast<const u32x4 *>(a.residual + row_off + (int64_t)vi[v] * 8);
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = pack_bf16x2(acc[v][2 * i] + bf16_elem(r, 2 * i),
+                                   acc[v][2 * i + 1] + bf16_elem(r, 2 * i + 1));
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xr = bf16_elem(o, e);     // the stored residual
+                acc[v][e] = xr;
+                ss = __builtin_fmaf(xr, xr, ss);
+            }
+            *reinterpret_cast<u32x4 *>(res_out + row_off + (int64_t)vi[v] * 8) = o;
+        }
+        const float tot = block_sum(ss, lds_red);
+        const float rstd = 1.0f / __builtin_sqrtf(tot / (float)a.H + a.eps);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            if (!ok[v]) continue;
+            const u32x4 gm = *reinterpret_cast<const u32x4 *>(a.gamma + (int64_t)vi[v] * 8);
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float g0 = bf16_elem(gm, 2 * i) + a.wb;
+                const float g1 = bf16_elem(gm, 2 * i + 1) + a.wb;
+                o[i] = pack_bf16x2((acc[v][2 * i] * rstd) * g0,
+                                   (acc[v][2 * i + 1] * rstd) * g1);
+            }
+            *reinterpret_cast<u32x4 *>(norm_out + row_off + (int64_t)vi[v] * 8) = o;
+        }
+    } else {
+        // flashinfer.comm.moe_a2a_combine, Parameters output_dtype
+        // (float8_e4m3fn) and output_scales (UE8M0, 32 elements per scale).
+        // A 32-element block is the 4 vectors of one DPP quad of lanes.
+        uint8_t *codes = static_cast<uint8_t *>(a.out0);
+        uint8_t *scales = static_cast<uint8_t *>(a.out1);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            int m = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                m = max(m, (int)(__float_as_uint(acc[v][e]) & 0x7FFFFFFFu));
+            m = quad_max(m);                            // all lanes active here
+            const unsigned ef = (unsigned)m >> 23;      // exponent field of amax
+            // scale byte = clamp(floor(log2 amax) - 8, -127, 127) + 127
+            const unsigned sbyte = ef == 255u ? 255u : (ef > 8u ? ef - 8u : 0u);
+            // 2^-e as an fp32 bit pattern, e = sbyte - 127 (e = 0 for NaN/inf)
+            const float inv = ef == 255u ? 1.0f : __uint_as_float((254u - sbyte) << 23);
+            if (!ok[v]) continue;
+            u32x2 o = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const unsigned sgn = (__float_as_uint(acc[v][e]) >> 24) & 0x80u;
+                const float q = acc[v][e] * inv;
+                const unsigned code = sgn | e4m3_mag(__float_as_uint(q) & 0x7FFFFFFFu);
+                o[e >> 2] |= code << ((e & 3) * 8);
+            }
+            *reinterpret_cast<u32x2 *>(codes + row_off + (int64_t)vi[v] * 8) = o;
+            if ((tid & 3) == 0)
+                scales[(int64_t)t * (a.H >> 5) + (vi[v] >> 2)] = (uint8_t)sbyte;
+        }
+    }
+}
+
+}  // namespace moe

@@ -1,0 +1,272 @@
+// Host side of the MoE expert-combine library: argument validation, launch
+// planning, kernel dispatch and the C ABI declared in include/moe_combine.h.
+//
+// Validation is pure host code and runs before any HIP call, so argument
+// errors are reported identically on machines without a GPU. The library
+// allocates nothing, keeps no state between calls and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "moe_combine.h"
+#include "combine_kernels.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+moe_status_t fail(moe_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status_t fail(moe_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status_t ok() {
+    g_err[0] = '\0';
+    return MOE_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int kMaxTopK = 32;
+constexpr int kMaxThreads = 1024;
+
+// Launch shape of one call.
+struct Plan {
+    int threads;   // workgroup size (multiple of 64)
+    int vec;       // 16-byte vectors per thread per chunk (1, 2, 4, 8)
+    int chunks;    // workgroups per token
+    int kt;        // slot tile (2, 4, 8)
+    bool masked;   // tail vectors past hidden/8 exist
+    int64_t blocks;
+};
+
+// Optional override "<threads>x<vectors>" for tuning sweeps.
+bool tile_override(int *threads, int *vec) {
+    const char *s = getenv("MOE_COMBINE_TILE");
+    if (!s || !*s || !strcmp(s, "auto")) return false;
+    int t = 0, v = 0;
+    if (sscanf(s, "%dx%d", &t, &v) != 2) return false;
+    if (t < 64 || t > kMaxThreads || t % 64 || !(v == 1 || v == 2 || v == 4 || v == 8)) return false;
+    *threads = t;
+    *vec = v;
+    return true;
+}
+
+moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
+    const int nvec = H / 8;
+    p->kt = k <= 2 ? 2 : (k <= 4 ? 4 : 8);
+    int threads = 0, vec = 0;
+    const bool forced = tile_override(&threads, &vec);
+    if (kind == moe::EPI_RMSNORM) {
+        // The row reduction needs the whole token in one workgroup.
+        if (!forced) {
+            vec = 0;
+            for (int v : {1, 2, 4, 8}) {
+                const int t = ((nvec + v - 1) / v + 63) / 64 * 64;
+                if (t <= 512 || (v == 8 && t <= kMaxThreads)) {
+                    vec = v;
+                    threads = t;
+                    break;
+                }
+            }
+            if (!vec) return fail(MOE_ERR_UNSUPPORTED, "hidden %d too large for the RMSNorm epilogue (max %d)", H, kMaxThreads * 8 * 8);
+        }
+        if ((int64_t)threads * vec < nvec)
+            return fail(MOE_ERR_UNSUPPORTED, "tile %dx%d does not cover hidden %d for RMSNorm", threads, vec, H);
+        p->chunks = 1;
+    } else {
+        if (!forced) {
+            vec = 1;
+            threads = nvec >= 128 ? 128 : 64;
+        }
+        p->chunks = (nvec + threads * vec - 1) / (threads * vec);
+    }
+    p->threads = threads;
+    p->vec = vec;
+    p->masked = (int64_t)p->chunks * threads * vec != nvec;
+    p->blocks = T * (int64_t)p->chunks;
+    if (p->blocks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large (%lld workgroups)", (long long)p->blocks);
+    return MOE_OK;
+}
+
+moe_status_t check_common(const void *payload, const int32_t *src_info, const float *w, const void *shared,
+                          int64_t T, int32_t H, int32_t k, int32_t ep, int64_t mtpr) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %lld)", (long long)T);
+    if (H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", H);
+    if (k < 1 || k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, %d] (got %d)", kMaxTopK, k);
+    if (ep < 1) return fail(MOE_ERR_INVALID_ARG, "ep_size must be >= 1 (got %d)", ep);
+    if (mtpr < 1 || mtpr > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "max_tokens_per_rank must be in [1, 2^31) (got %lld)", (long long)mtpr);
+    if (T > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be < 2^31");
+    if ((double)ep * (double)mtpr * (double)H * 2.0 > 9.0e18) return fail(MOE_ERR_INVALID_ARG, "payload size overflows");
+    if (T == 0) return MOE_OK;
+    if (!payload) return fail(MOE_ERR_INVALID_ARG, "payload is NULL");
+    if (!src_info) return fail(MOE_ERR_INVALID_ARG, "src_info is NULL");
+    if (!aligned(payload, 16)) return fail(MOE_ERR_INVALID_ARG, "payload must be 16-byte aligned");
+    if (!aligned(src_info, 8)) return fail(MOE_ERR_INVALID_ARG, "src_info must be 8-byte aligned");
+    if (w && !aligned(w, 4)) return fail(MOE_ERR_INVALID_ARG, "router_weights must be 4-byte aligned");
+    if (shared && !aligned(shared, 16)) return fail(MOE_ERR_INVALID_ARG, "shared_out must be 16-byte aligned");
+    return MOE_OK;
+}
+
+template <int KT, int V, int EPI, bool MASK>
+void launch_one(const Plan &p, const moe::KernelArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL((moe::combine_kernel<KT, V, EPI, MASK>), dim3((unsigned)p.blocks), dim3(p.threads), 0, s, a);
+}
+
+template <int KT, int V, int EPI>
+void launch_mask(const Plan &p, const moe::KernelArgs &a, hipStream_t s) {
+    if (p.masked) launch_one<KT, V, EPI, true>(p, a, s);
+    else launch_one<KT, V, EPI, false>(p, a, s);
+}
+
+template <int KT, int EPI>
+void launch_vec(const Plan &p, const moe::KernelArgs &a, hipStream_t s) {
+    switch (p.vec) {
+        case 1: launch_mask<KT, 1, EPI>(p, a, s); break;
+        case 2: launch_mask<KT, 2, EPI>(p, a, s); break;
+        case 4: launch_mask<KT, 4, EPI>(p, a, s); break;
+        default: launch_mask<KT, 8, EPI>(p, a, s); break;
+    }
+}
+
+template <int EPI>
+moe_status_t launch(const Plan &p, const moe::KernelArgs &a, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (p.kt) {
+        case 2: launch_vec<2, EPI>(p, a, s); break;
+        case 4: launch_vec<4, EPI>(p, a, s); break;
+        default: launch_vec<8, EPI>(p, a, s); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+moe::KernelArgs base_args(const void *payload, const int32_t *src_info, const float *w, const void *shared,
+                          int32_t H, int32_t k, int64_t mtpr, const Plan &p) {
+    moe::KernelArgs a;
+    memset(&a, 0, sizeof a);
+    a.payload = static_cast<const uint16_t *>(payload);
+    a.src_info = src_info;
+    a.weights = w;
+    a.shared = static_cast<const uint16_t *>(shared);
+    a.mtpr = mtpr;
+    a.H = H;
+    a.nvec = H / 8;
+    a.k = k;
+    a.chunks = p.chunks;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_combine_abi_version(void) { return MOE_COMBINE_ABI_VERSION; }
+
+const char *moe_combine_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char *moe_combine_last_error(void) { return g_err; }
+
+moe_status_t moe_combine(const void *payload, const int32_t *src_info, const float *router_weights,
+                         const void *shared_out, void *out, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                         int32_t ep_size, int64_t max_tokens_per_rank, void *stream) {
+    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
+                                   ep_size, max_tokens_per_rank);
+    if (st != MOE_OK) return st;
+    if (num_tokens == 0) return ok();
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if (out == payload || out == shared_out) return fail(MOE_ERR_INVALID_ARG, "out must not alias an input");
+    Plan p;
+    if ((st = make_plan(moe::EPI_BF16, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    a.out0 = out;
+    return launch<moe::EPI_BF16>(p, a, stream);
+}
+
+moe_status_t moe_combine_residual_rmsnorm(const void *payload, const int32_t *src_info, const float *router_weights,
+                                          const void *shared_out, const void *residual_in, const void *gamma,
+                                          float eps, float weight_bias, void *residual_out, void *norm_out,
+                                          int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t ep_size,
+                                          int64_t max_tokens_per_rank, void *stream) {
+    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
+                                   ep_size, max_tokens_per_rank);
+    if (st != MOE_OK) return st;
+    Plan p;
+    if ((st = make_plan(moe::EPI_RMSNORM, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    if (num_tokens == 0) return ok();
+    if (!residual_in || !gamma || !residual_out || !norm_out)
+        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out are required");
+    if (!aligned(residual_in, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) || !aligned(norm_out, 16))
+        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out must be 16-byte aligned");
+    if (norm_out == residual_out || norm_out == residual_in)
+        return fail(MOE_ERR_INVALID_ARG, "norm_out must differ from residual_in and residual_out");
+    const void *outs[2] = {residual_out, norm_out};
+    for (const void *o : outs)
+        if (o == payload || o == shared_out || o == gamma) return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input");
+    if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    a.residual = static_cast<const uint16_t *>(residual_in);
+    a.gamma = static_cast<const uint16_t *>(gamma);
+    a.out0 = residual_out;
+    a.out1 = norm_out;
+    a.eps = eps;
+    a.wb = weight_bias;
+    return launch<moe::EPI_RMSNORM>(p, a, stream);
+}
+
+moe_status_t moe_combine_mxfp8(const void *payload, const int32_t *src_info, const float *router_weights,
+                               const void *shared_out, void *out_fp8, uint8_t *out_scales, int64_t num_tokens,
+                               int32_t hidden, int32_t top_k, int32_t ep_size, int64_t max_tokens_per_rank,
+                               void *stream) {
+    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
+                                   ep_size, max_tokens_per_rank);
+    if (st != MOE_OK) return st;
+    if (hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8 (got %d)", hidden);
+    if (num_tokens == 0) return ok();
+    if (!out_fp8 || !out_scales) return fail(MOE_ERR_INVALID_ARG, "out_fp8 and out_scales are required");
+    if (!aligned(out_fp8, 8)) return fail(MOE_ERR_INVALID_ARG, "out_fp8 must be 8-byte aligned");
+    if (out_fp8 == payload || out_fp8 == shared_out || (const void *)out_scales == payload ||
+        (const void *)out_scales == shared_out || (const void *)out_scales == out_fp8)
+        return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input or each other");
+    Plan p;
+    if ((st = make_plan(moe::EPI_MXFP8, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    a.out0 = out_fp8;
+    a.out1 = out_scales;
+    return launch<moe::EPI_MXFP8>(p, a, stream);
+}
+
+moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,
+                                         int32_t buflen) {
+    if (kind < 0 || kind > 2) return fail(MOE_ERR_INVALID_ARG, "kind must be 0, 1 or 2");
+    if (!buf || buflen < 1) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or empty");
+    moe_status_t st = check_common(reinterpret_cast<const void *>(16), reinterpret_cast<const int32_t *>(16), nullptr,
+                                   nullptr, num_tokens, hidden, top_k, 1, 1);
+    if (st != MOE_OK) return st;
+    if (kind == 2 && hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8");
+    Plan p;
+    if ((st = make_plan(kind, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    snprintf(buf, (size_t)buflen, "threads=%d vec_per_thread=%d chunks=%d blocks=%lld slot_tile=%d masked=%d",
+             p.threads, p.vec, p.chunks, (long long)p.blocks, p.kt, (int)p.masked);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+"""C-ABI library: loads, exports every declared symbol, rejects bad arguments
+before touching the GPU (no compute call is made here), fails loudly when
+missing, and shares no code with the oracle. Runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import moe_expert_combine_amd as mc
+from moe_expert_combine_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_combine.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_combine\w*)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
+              "moe_combine_describe_launch", "moe_combine_abi_version",
+              "moe_combine_status_string", "moe_combine_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = mc.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert mc.abi_version() == 1
+
+
+def test_status_strings():
+    L = mc.lib()
+    assert L.moe_combine_status_string(0) == b"MOE_OK"
+    assert L.moe_combine_status_string(1) == b"MOE_ERR_INVALID_ARG"
+    assert L.moe_combine_status_string(3) == b"MOE_ERR_HIP"
+    assert L.moe_combine_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+# Fake, well-aligned device addresses: every call below is rejected (or is a
+# zero-token no-op) before any HIP call, so nothing is dereferenced.
+A = 1 << 20
+
+
+def call_combine(payload=A, src=A, w=A, shared=None, out=2 * A, T=4, H=64, k=2,
+                 ep=1, mtpr=8):
+    return mc.lib().moe_combine(payload, src, w, shared, out, T, H, k, ep, mtpr, None)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(T=-1), "num_tokens"),
+    (dict(H=0), "hidden"),
+    (dict(H=12), "hidden"),
+    (dict(k=0), "top_k"),
+    (dict(k=33), "top_k"),
+    (dict(ep=0), "ep_size"),
+    (dict(mtpr=0), "max_tokens_per_rank"),
+    (dict(payload=None), "payload"),
+    (dict(src=None), "src_info"),
+    (dict(out=None), "out"),
+    (dict(payload=A + 8), "aligned"),
+    (dict(src=A + 4), "aligned"),
+    (dict(w=A + 2), "aligned"),
+    (dict(out=A + 8), "aligned"),
+    (dict(shared=A + 8), "aligned"),
+    (dict(out=A), "alias"),
+])
+def test_moe_combine_rejects_bad_arguments(kw, msg):
+    assert call_combine(**kw) == INVALID
+    assert msg in mc.lib().moe_combine_last_error().decode()
+
+
+def test_zero_tokens_is_a_no_op():
+    assert call_combine(T=0, out=None, payload=None, src=None) == OK
+    L = mc.lib()
+    assert L.moe_combine_mxfp8(None, None, None, None, None, None, 0, 64, 2, 1, 8, None) == OK
+    assert L.moe_combine_residual_rmsnorm(None, None, None, None, None, None, 1e-6, 0.0,
+                                          None, None, 0, 64, 2, 1, 8, None) == OK
+
+
+def test_rmsnorm_argument_errors():
+    L = mc.lib()
+    f = lambda ro, no, res=3 * A, g=4 * A, eps=1e-6: L.moe_combine_residual_rmsnorm(
+        A, A, A, None, res, g, eps, 0.0, ro, no, 4, 64, 2, 1, 8, None)
+    assert f(5 * A, 5 * A) == INVALID            # residual_out == norm_out
+    assert f(5 * A, 3 * A) == INVALID            # norm_out == residual_in
+    assert f(None, 6 * A) == INVALID
+    assert f(5 * A, 6 * A, g=None) == INVALID
+    assert f(5 * A, 6 * A, eps=-1.0) == INVALID
+    assert f(5 * A + 2, 6 * A) == INVALID
+
+
+def test_mxfp8_argument_errors():
+    L = mc.lib()
+    f = lambda H=64, o=5 * A, s=6 * A: L.moe_combine_mxfp8(A, A, A, None, o, s, 4, H, 2, 1, 8, None)
+    assert f(H=40) == INVALID                    # not a multiple of 32
+    assert "multiple of 32" in L.moe_combine_last_error().decode()
+    assert f(o=None) == INVALID
+    assert f(s=None) == INVALID
+    assert f(o=5 * A + 4) == INVALID
+    assert f(s=5 * A) == INVALID                 # scales alias codes
+
+
+def test_describe_launch_shapes():
+    d = mc.describe_launch(0, 4096, 7168, 8)
+    assert "chunks=7" in d and "blocks=28672" in d and "masked=0" in d
+    d = mc.describe_launch(1, 2048, 7168, 8)
+    assert "threads=448 vec_per_thread=2 chunks=1" in d
+    d = mc.describe_launch(2, 16384, 7168, 8)
+    assert "masked=0" in d
+    d = mc.describe_launch(0, 5, 264, 3)          # ragged: 33 vectors
+    assert "masked=1" in d and "slot_tile=4" in d
+    with pytest.raises(mc.MoeCombineError):
+        mc.describe_launch(2, 4, 48, 2)
+    with pytest.raises(mc.MoeCombineError):
+        mc.describe_launch(1, 4, 8 * 8 * 1024 + 8, 2)
+
+
+def test_tile_override_env(monkeypatch):
+    monkeypatch.setenv("MOE_COMBINE_TILE", "256x2")
+    assert "threads=256 vec_per_thread=2 chunks=2" in mc.describe_launch(0, 10, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "64x1")
+    with pytest.raises(mc.MoeCombineError):      # RMSNorm needs the whole row
+        mc.describe_launch(1, 10, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "100x3")   # invalid -> ignored
+    assert "threads=128" in mc.describe_launch(0, 10, 7168, 8)
+
+
+def test_binding_rejects_host_tensors_and_bad_dtypes():
+    p = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    s = torch.zeros((2, 1, 2), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mc.moe_combine(p, s)
+    with pytest.raises(ValueError):
+        mc.moe_combine_mxfp8(p.float(), s)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library (and no compiler) calls raise."""
+    monkeypatch.setattr(_build, "LIB", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_build, "HIPCC", str(tmp_path / "no-hipcc"))
+    monkeypatch.setattr(mc, "_lib", None)
+    with pytest.raises(Exception):
+        mc.lib()
+
+
+def _py_sources(d):
+    for dp, _, fs in os.walk(os.path.join(ROOT, d)):
+        for f in fs:
+            if f.endswith((".py", ".hip", ".h", ".c", ".cpp")):
+                yield os.path.join(dp, f)
+
+
+def test_product_and_oracle_share_no_code():
+    for f in _py_sources("moe_expert_combine_amd"):
+        txt = open(f).read()
+        assert not re.search(r"\boracle\b", txt), f
+    for f in _py_sources("oracle"):
+        txt = open(f).read()
+        assert "moe_expert_combine_amd" not in txt and "combine_kernels" not in txt, f
+        assert "import gen" not in txt, f
+    for f in _py_sources("gen"):
+        txt = open(f).read()
+        assert "import oracle" not in txt and "moe_expert_combine_amd" not in txt, f

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Acceptance, per output:
+  * bf16 outputs (combine, residual_out, norm_out): at most one bf16 step
+    apart on the monotone integer line, NaN only where the oracle has NaN.
+    The combine and residual_out take the same fp32 operations in the same
+    order as the oracle, so they are also required to be identical on all
+    but 0.1% of elements; norm_out differs from the oracle's double-precision
+    statistic only by rounding, and is required identical on all but 1%.
+  * MXFP8 scales: bit-exact.
+  * e4m3 codes: at most one code step apart, on at most 0.1% of elements.
+Outputs are poisoned first, so every element the kernel should write is
+checked, and rows past num_tokens must keep the poison.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import moe_expert_combine_amd as mc
+from tests.test_oracle_pins import load_fixture, to_bf16_bits, ulp_dist_bf16
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+POISON16 = 0xFFFF      # a NaN pattern the kernels never produce from finite data
+POISON8 = 0xEE
+
+
+def dev16(a):
+    """uint16 numpy bits -> bf16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_dev(inp):
+    d = dict(payload=dev16(inp.payload),
+             src_info=torch.from_numpy(inp.src_info).to(DEV),
+             weights=None if inp.weights is None else torch.from_numpy(inp.weights).to(DEV),
+             shared=None if inp.shared is None else dev16(inp.shared))
+    if inp.residual is not None:
+        d["residual"] = dev16(inp.residual)
+        d["gamma"] = dev16(inp.gamma)
+    return d
+
+
+def poisoned16(T, H, extra=0):
+    return torch.full((T + extra, H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+
+
+def check_bf16(got, ref, exact_frac, what):
+    d = ulp_dist_bf16(got, ref)
+    assert d.max() <= 1, f"{what}: max ulp distance {d.max()}"
+    frac = (d != 0).mean() if d.size else 0.0
+    assert frac <= exact_frac, f"{what}: {frac:.2e} of elements differ by one step"
+
+
+def e4m3_step_dist(a, b):
+    """Distance in e4m3 code steps on the monotone line (NaN codes excluded)."""
+    def key(c):
+        c = c.astype(np.int32)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+    return np.abs(key(a) - key(b))
+
+
+def check_mxfp8(codes, scales, rc, rs, what):
+    np.testing.assert_array_equal(scales, rs, err_msg=f"{what}: scales")
+    nan_g = (codes & 0x7F) == 0x7F
+    nan_r = (rc & 0x7F) == 0x7F
+    np.testing.assert_array_equal(nan_g, nan_r, err_msg=f"{what}: NaN codes")
+    d = e4m3_step_dist(codes[~nan_g], rc[~nan_g])
+    assert d.max(initial=0) <= 1, f"{what}: code distance {d.max()}"
+    assert (d != 0).mean() <= 1e-3 if d.size else True, f"{what}: too many off-by-one codes"
+
+
+# ----------------------------------------------------------------- runners
+
+def run_combine(inp, extra_rows=0):
+    d = to_dev(inp)
+    out = poisoned16(inp.T, inp.H, extra_rows)
+    mc.moe_combine(d["payload"], d["src_info"], d["weights"], d["shared"], out=out)
+    torch.cuda.synchronize()
+    o = host16(out)
+    if extra_rows:
+        assert (o[inp.T:] == POISON16).all(), "rows past num_tokens were written"
+    return o[:inp.T]
+
+
+def run_rmsnorm(inp, wb, extra_rows=0, in_place=False):
+    d = to_dev(inp)
+    norm = poisoned16(inp.T, inp.H, extra_rows)
+    if in_place:
+        ro = torch.cat([d["residual"], poisoned16(0, inp.H, extra_rows)]) if extra_rows else d["residual"]
+        res_in = ro
+    else:
+        ro = poisoned16(inp.T, inp.H, extra_rows)
+        res_in = d["residual"]
+    mc.moe_combine_residual_rmsnorm(d["payload"], d["src_info"], d["weights"], d["shared"],
+                                    res_in, d["gamma"], inp.eps, wb,
+                                    residual_out=ro, norm_out=norm)
+    torch.cuda.synchronize()
+    a, b = host16(ro), host16(norm)
+    if extra_rows:
+        assert (a[inp.T:] == POISON16).all() and (b[inp.T:] == POISON16).all()
+    return a[:inp.T], b[:inp.T]
+
+
+def run_mxfp8(inp, extra_rows=0):
+    d = to_dev(inp)
+    T, H = inp.T, inp.H
+    codes = torch.full((T + extra_rows, H), POISON8, dtype=torch.uint8, device=DEV)
+    scales = torch.full((T + extra_rows, H // 32), POISON8, dtype=torch.uint8, device=DEV)
+    mc.moe_combine_mxfp8(d["payload"], d["src_info"], d["weights"], d["shared"],
+                         out_fp8=codes.view(torch.float8_e4m3fn), out_scales=scales)
+    torch.cuda.synchronize()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    if extra_rows:
+        assert (c[T:] == POISON8).all() and (s[T:] == POISON8).all()
+    return c[:T], s[:T]
+
+
+def oracle_all(inp, kind, wb=0.0):
+    if kind == "bf16":
+        return oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared)
+    if kind == "rmsnorm":
+        return oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
+                                               inp.shared, inp.residual, inp.gamma,
+                                               inp.eps, wb)
+    return oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights, inp.shared)
+
+
+def check_all_kinds(inp, wbs=(0.0, 1.0), extra_rows=3, what=""):
+    check_bf16(run_combine(inp, extra_rows), oracle_all(inp, "bf16"), 1e-3, f"{what} combine")
+    if inp.residual is not None:
+        for wb in wbs:
+            ro, no = run_rmsnorm(inp, wb, extra_rows)
+            rro, rno = oracle_all(inp, "rmsnorm", wb)
+            check_bf16(ro, rro, 1e-3, f"{what} residual_out wb={wb}")
+            check_bf16(no, rno, 1e-2, f"{what} norm_out wb={wb}")
+    if inp.H % 32 == 0:
+        c, s = run_mxfp8(inp, extra_rows)
+        rc, rs = oracle_all(inp, "mxfp8")
+        check_mxfp8(c, s, rc, rs, f"{what} mxfp8")
+
+
+def with_norm_inputs(c):
+    c = dict(c)
+    c.setdefault("residual_sd", 1.0)
+    c.setdefault("gamma_sd", 0.1)
+    return c
+
+
+# --------------------------------------------------------------- fixtures
+
+def test_golden_fixtures_on_gpu():
+    """The hand-worked examples, through the HIP path."""
+    fx = load_fixture("combine_small.txt")
+    dd = fx["dims"]
+    payload = np.zeros((dd["ep"], dd["mtpr"], dd["H"]), np.uint16)
+    for (r, row), vals in fx["rows"].items():
+        payload[r, row] = to_bf16_bits(vals)
+    src = np.full((dd["T"], dd["k"], 2), -1, np.int32)
+    w = np.zeros((dd["T"], dd["k"]), np.float32)
+    for (t, j), (r, row, wj) in fx["slots"].items():
+        src[t, j] = (r, row)
+        w[t, j] = wj
+    out = mc.moe_combine(dev16(payload), torch.from_numpy(src).to(DEV),
+                         torch.from_numpy(w).to(DEV))
+    o = host16(out)
+    for t, vals in fx["expect"].items():
+        np.testing.assert_array_equal(o[t], to_bf16_bits(vals))
+
+    fx = load_fixture("rmsnorm_small.txt")
+    payload = np.zeros((1, 1, 8), np.uint16)
+    payload[0, 0] = to_bf16_bits(fx["rows"][(0, 0)])
+    src = torch.zeros((1, 1, 2), dtype=torch.int32, device=DEV)
+    w = torch.ones((1, 1), dtype=torch.float32, device=DEV)
+    res = dev16(to_bf16_bits(fx["residual"][0])[None])
+    g = dev16(to_bf16_bits(fx["gamma"]))
+    for case in fx["cases"]:
+        ro, no = mc.moe_combine_residual_rmsnorm(dev16(payload), src, w, None, res, g,
+                                                 case["eps"], case["weight_bias"])
+        np.testing.assert_array_equal(host16(ro)[0], to_bf16_bits(fx["expect_residual"][0]))
+        np.testing.assert_array_equal(host16(no)[0], to_bf16_bits(case["norm"][0]),
+                                      err_msg=case["name"])
+
+    fx = load_fixture("mxfp8_small.txt")
+    x0 = np.array(fx["x"][0], dtype=np.float32)
+    payload = np.stack([to_bf16_bits(x0), to_bf16_bits(-x0)])[None]
+    src = torch.tensor([[[0, 0]], [[0, 1]]], dtype=torch.int32, device=DEV)
+    w = torch.ones((2, 1), dtype=torch.float32, device=DEV)
+    codes, scales = mc.moe_combine_mxfp8(dev16(payload), src, w)
+    codes = codes.view(torch.uint8).cpu().numpy()
+    scales = scales.cpu().numpy()
+    for t in range(2):
+        assert list(scales[t]) == fx["scales"][t]
+        assert list(codes[t]) == fx["codes"][t]
+
+
+# ------------------------------------------------------------ small shapes
+
+def test_tiny_config_all_outputs():
+    check_all_kinds(gen.make_inputs(with_norm_inputs(gen.CONFIGS["tiny"]), 0), what="tiny")
+
+
+@pytest.mark.parametrize("T,H,k,ep,extra", [
+    (1, 8, 1, 1, {}),                       # one vector, one slot
+    (7, 264, 3, 2, {}),                     # ragged hidden (33 vectors), odd top_k
+    (33, 1032, 5, 3, dict(drop_frac=0.3)),  # ragged tail past one chunk, drops
+    (65, 4096, 8, 8, dict(shared_sd=0.5)),  # shared expert, exact tiles
+    (17, 7168, 8, 8, dict(drop_frac=0.5, shared_sd=0.5)),
+    (9, 2048, 13, 4, {}),                   # top_k > 8: two slot groups
+    (5, 512, 32, 8, dict(drop_frac=0.2)),   # maximum top_k
+    (40, 96, 2, 1, dict(weights=False)),    # unit weights (no router weights)
+])
+def test_ragged_and_edge_shapes(T, H, k, ep, extra):
+    c = with_norm_inputs(dict(T=T, H=H, E=max(k, 8) * ep, ep=ep, k=k, **extra))
+    check_all_kinds(gen.make_inputs(c, seed=T), what=f"T={T} H={H} k={k}")
+
+
+def test_unoccupied_nan_rows_and_all_dropped_tokens():
+    c = with_norm_inputs(dict(T=48, H=1024, E=32, ep=4, k=8, unoccupied="nan",
+                              drop_frac=0.4, shared_sd=0.5))
+    inp = gen.make_inputs(c, seed=4, mtpr=1024)
+    inp.src_info[5] = -1                     # token 5: every slot dropped
+    inp.src_info[6] = -1
+    inp.shared[6] = 0                        # token 6: dropped, zero shared
+    check_all_kinds(inp, what="nan rows")
+    out = run_combine(inp)
+    assert not ((out & 0x7FFF) > 0x7F80).any()
+
+
+def test_all_slots_dropped_without_shared_gives_plus_zero():
+    inp = gen.make_inputs(dict(T=12, H=256, E=8, ep=2, k=4), seed=1)
+    inp.src_info[:] = -1
+    assert (run_combine(inp) == 0).all()
+    c, s = run_mxfp8(inp)
+    assert (c == 0).all() and (s == 0).all()
+
+
+def test_zero_tokens_leaves_outputs_untouched():
+    inp = gen.make_inputs(dict(T=4, H=64, E=8, ep=1, k=2), seed=0)
+    d = to_dev(inp)
+    out = poisoned16(0, 64, 3)
+    mc.moe_combine(d["payload"], d["src_info"][:0], d["weights"][:0], out=out)
+    torch.cuda.synchronize()
+    assert (host16(out) == POISON16).all()
+
+
+def test_in_place_residual_update():
+    inp = gen.make_inputs(with_norm_inputs(dict(T=20, H=7168, E=64, ep=8, k=8)), seed=9)
+    ro, no = run_rmsnorm(inp, 1.0, in_place=True)
+    rro, rno = oracle_all(inp, "rmsnorm", 1.0)
+    check_bf16(ro, rro, 1e-3, "in-place residual_out")
+    check_bf16(no, rno, 1e-2, "in-place norm_out")
+
+
+def test_layout_invariance_on_gpu():
+    """Same (token, slot) rows under another ep_size / row order: identical."""
+    rng = np.random.default_rng(3)
+    T, H, E, k = 64, 2048, 32, 8
+    rows = to_bf16_bits(rng.standard_normal((T, k, H)).astype(np.float32))
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = torch.from_numpy(rng.random((T, k)).astype(np.float32)).to(DEV)
+    outs = []
+    for ep in (1, 4, 8):
+        src, loads = gen.dispatch_slots(topk, np.zeros((T, k), bool), E, ep, None)
+        payload = gen.scatter_rows(src, rows, ep, int(loads.max()) + 3)
+        outs.append(host16(mc.moe_combine(dev16(payload), torch.from_numpy(src).to(DEV), w)))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+
+
+def test_e4m3_conversion_every_bf16_pattern():
+    """All 65536 bf16 patterns as single-slot sums (so acc is exactly each
+    pattern), blocks of 32 consecutive patterns: the kernel's integer e4m3 and
+    UE8M0 route against the oracle, NaN/inf blocks included."""
+    H = 1024
+    allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(64, H)
+    rng = np.random.default_rng(0)
+    shuffled = rng.permutation(allp.reshape(-1)).reshape(64, H)
+    payload = np.concatenate([allp, shuffled])[None]
+    T = payload.shape[1]
+    src = np.stack([np.zeros(T, np.int32), np.arange(T, dtype=np.int32)], axis=-1)[:, None, :]
+    src = np.ascontiguousarray(src)
+    w = np.ones((T, 1), np.float32)
+    codes, scales = mc.moe_combine_mxfp8(dev16(payload), torch.from_numpy(src).to(DEV),
+                                         torch.from_numpy(w).to(DEV))
+    codes = codes.view(torch.uint8).cpu().numpy()
+    rc, rs = oracle.combine_mxfp8(payload, src, w)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes, rc)
+
+
+@pytest.mark.parametrize("tile", ["64x1", "64x2", "128x2", "256x1", "256x4", "512x8",
+                                  "1024x1", "448x2", "896x1", "192x8"])
+def test_every_tile_shape(monkeypatch, tile):
+    """Each launch shape the tile override can pick computes the same result."""
+    monkeypatch.setenv("MOE_COMBINE_TILE", tile)
+    c = with_norm_inputs(dict(T=19, H=7168, E=64, ep=8, k=6, drop_frac=0.1, shared_sd=0.5))
+    inp = gen.make_inputs(c, seed=2)
+    nt, v = (int(x) for x in tile.split("x"))
+    check_bf16(run_combine(inp, 2), oracle_all(inp, "bf16"), 1e-3, tile)
+    c_, s_ = run_mxfp8(inp, 2)
+    check_mxfp8(c_, s_, *oracle_all(inp, "mxfp8"), tile)
+    if nt * v * 8 >= inp.H:
+        ro, no = run_rmsnorm(inp, 0.0, 2)
+        rro, rno = oracle_all(inp, "rmsnorm", 0.0)
+        check_bf16(ro, rro, 1e-3, tile)
+        check_bf16(no, rno, 1e-2, tile)
+
+
+# ----------------------------------------------- full workload sizes
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["dsv3", "skewed", "rmsnorm", "mxfp8"])
+def test_full_size_workloads(name):
+    """The full synthetic workloads in the launch configuration the benchmark
+    times, compared element by element with the oracle."""
+    inp = gen.make_inputs(name, 0)
+    if name == "rmsnorm":
+        for wb in (0.0, 1.0):
+            ro, no = run_rmsnorm(inp, wb)
+            rro, rno = oracle_all(inp, "rmsnorm", wb)
+            check_bf16(ro, rro, 1e-3, f"{name} residual_out wb={wb}")
+            check_bf16(no, rno, 1e-2, f"{name} norm_out wb={wb}")
+    elif name == "mxfp8":
+        c, s = run_mxfp8(inp)
+        check_mxfp8(c, s, *oracle_all(inp, "mxfp8"), name)
+    else:
+        check_bf16(run_combine(inp), oracle_all(inp, "bf16"), 1e-3, name)
