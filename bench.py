@@ -3,9 +3,9 @@
 A step is one combine over one batch of synthetic inputs already resident in
 HBM. Several identical copies of the inputs and outputs are rotated from step
 to step, so no launch finds its payload in the 256 MB Infinity Cache or L2
-left by the previous one. Every launch in the timed region is bracketed by
-HIP events on the stream it runs on; their mean is the kernel duration used
-for the roofline. ``value`` is tokens per second of wall-clock time over the
+left by the previous one. Two HIP events on the launch stream bracket the K
+launches of the timed region; elapsed / K is the kernel duration used for the
+roofline. ``value`` is tokens per second of wall-clock time over the
 timed region.
 
 Default workload: T=4096, hidden=7168, top_k=8, 256 experts over 8 simulated
@@ -50,6 +50,9 @@ def parse():
                     help="input copies rotated per step (0: enough for >= 1.5 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, run 5 device copies of MIB MiB (a plain copy kernel "
+                         "of known size, to calibrate profiler byte counters)")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per launch of the kernel")
     return ap.parse_args()
@@ -132,23 +135,44 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    # timed region: K back-to-back launches between two events on the launch
+    # stream; their mean is the kernel duration the roofline uses
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step(args.warmup + i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kms = np.array([a.elapsed_time(b) for a, b in ev])
-    kernel_ms = float(kms.mean())
+    kernel_ms = e0.elapsed_time(e1) / K
     ms_per_step = wall * 1e3 / K
     tokens_per_s = T * K / wall
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
-    print(f"[bench] kernel mean {kernel_ms * 1e3:.1f} us (p10 {np.percentile(kms, 10) * 1e3:.1f}, "
-          f"p90 {np.percentile(kms, 90) * 1e3:.1f}), {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    # spread only: a short pass with an event pair around every launch (the
+    # extra event packets add a few microseconds to each sample)
+    n_sp = min(K, 100)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_sp)]
+    for i in range(n_sp):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    print(f"[bench] kernel mean {kernel_ms * 1e3:.1f} us over the timed region; per-launch "
+          f"p10 {np.percentile(kms, 10) * 1e3:.1f} p90 {np.percentile(kms, 90) * 1e3:.1f} us; "
+          f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        src_t = torch.empty(args.copy_probe << 19, dtype=torch.int16, device=dev).fill_(3)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(5):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: 5 x {args.copy_probe} MiB device copies", file=sys.stderr, flush=True)
+        del src_t, dst_t
 
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
@@ -194,7 +218,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": algo_bytes,
-                     "kernel_us_mean": kernel_ms * 1e3},
+                     "kernel_us_mean": kernel_ms * 1e3,
+                     "kernel_us_p10_p90_per_launch_events": [float(np.percentile(kms, 10) * 1e3),
+                                                             float(np.percentile(kms, 90) * 1e3)]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -112,7 +112,9 @@ def test_mxfp8_argument_errors():
 
 def test_describe_launch_shapes():
     d = mc.describe_launch(0, 4096, 7168, 8)
-    assert "chunks=7" in d and "blocks=28672" in d and "masked=0" in d
+    assert "threads=64 vec_per_thread=2 chunks=7 blocks=28672 slot_tile=8 masked=0" == d
+    d = mc.describe_launch(0, 100, 4096, 8)
+    assert "chunks=4" in d and "masked=0" in d
     d = mc.describe_launch(1, 2048, 7168, 8)
     assert "threads=448 vec_per_thread=2 chunks=1" in d
     d = mc.describe_launch(2, 16384, 7168, 8)
@@ -122,7 +124,9 @@ def test_describe_launch_shapes():
     with pytest.raises(mc.MoeCombineError):
         mc.describe_launch(2, 4, 48, 2)
     with pytest.raises(mc.MoeCombineError):
-        mc.describe_launch(1, 4, 8 * 8 * 1024 + 8, 2)
+        mc.describe_launch(1, 4, 8 * 8 * 512 + 8, 2)
+    assert "threads=512 vec_per_thread=8" in mc.describe_launch(1, 4, 8 * 8 * 512, 2)
+    assert "slot_tile=2" in mc.describe_launch(1, 4, 8 * 8 * 512, 8)
 
 
 def test_tile_override_env(monkeypatch):
@@ -131,8 +135,12 @@ def test_tile_override_env(monkeypatch):
     monkeypatch.setenv("MOE_COMBINE_TILE", "64x1")
     with pytest.raises(mc.MoeCombineError):      # RMSNorm needs the whole row
         mc.describe_launch(1, 10, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "128x4")
+    assert "slot_tile=4" in mc.describe_launch(0, 10, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "1024x4")  # over the V>=4 budget -> ignored
+    assert "threads=64 vec_per_thread=2" in mc.describe_launch(0, 10, 7168, 8)
     monkeypatch.setenv("MOE_COMBINE_TILE", "100x3")   # invalid -> ignored
-    assert "threads=128" in mc.describe_launch(0, 10, 7168, 8)
+    assert "threads=64 vec_per_thread=2" in mc.describe_launch(0, 10, 7168, 8)
 
 
 def test_binding_rejects_host_tensors_and_bad_dtypes():

@@ -218,6 +218,8 @@ def test_tiny_config_all_outputs():
     (9, 2048, 13, 4, {}),                   # top_k > 8: two slot groups
     (5, 512, 32, 8, dict(drop_frac=0.2)),   # maximum top_k
     (40, 96, 2, 1, dict(weights=False)),    # unit weights (no router weights)
+    (3, 30000, 8, 8, {}),                   # wide row: RMSNorm with 8 vectors/lane
+    (2, 32768, 4, 2, dict(shared_sd=0.5)),  # widest RMSNorm row supported
 ])
 def test_ragged_and_edge_shapes(T, H, k, ep, extra):
     c = with_norm_inputs(dict(T=T, H=H, E=max(k, 8) * ep, ep=ep, k=k, **extra))
@@ -298,8 +300,8 @@ def test_e4m3_conversion_every_bf16_pattern():
     np.testing.assert_array_equal(codes, rc)
 
 
-@pytest.mark.parametrize("tile", ["64x1", "64x2", "128x2", "256x1", "256x4", "512x8",
-                                  "1024x1", "448x2", "896x1", "192x8"])
+@pytest.mark.parametrize("tile", ["64x1", "64x2", "64x4", "128x2", "128x4", "256x1", "256x4",
+                                  "512x8", "512x4", "1024x1", "448x2", "896x1", "192x8", "1024x2"])
 def test_every_tile_shape(monkeypatch, tile):
     """Each launch shape the tile override can pick computes the same result."""
     monkeypatch.setenv("MOE_COMBINE_TILE", tile)
