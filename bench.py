@@ -39,6 +39,21 @@ DESCR = {
 }
 
 
+def kernel_source_hash():
+    """sha256 over the kernel and ABI sources; byte counters taken from an
+    older kernel are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_expert_combine_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    files.append(os.path.join(ROOT, "include", "moe_combine.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -54,7 +69,8 @@ def parse():
                     help="after timing, run 5 device copies of MIB MiB (a plain copy kernel "
                          "of known size, to calibrate profiler byte counters)")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the kernel")
+                    help="JSON with measured HBM bytes per launch (default: "
+                         "profiles/traffic_<workload>.json)")
     return ap.parse_args()
 
 
@@ -175,10 +191,12 @@ def main():
         del src_t, dst_t
 
     traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
+    tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
             tr = json.load(f)
-        if tr.get("workload") == args.workload:
+        if (tr.get("workload") == args.workload
+                and tr.get("kernel_source_sha256") == kernel_source_hash()):
             traffic = tr.get("bytes_per_launch")
 
     cpu = None
