@@ -13,6 +13,8 @@ the documentation pages it follows, is stated in ``oracle.c``:
                                    shared expert, RNE to bf16);
 * ``combine_residual_rmsnorm``  -- + residual add and RMSNorm (weight_bias);
 * ``combine_mxfp8``             -- + MXFP8 e4m3 codes and UE8M0 scales / 32;
+* ``combine_residual_rmsnorm_mxfp8`` -- RMSNorm whose normalised row is also
+                                   quantised to MXFP8;
 * ``routed_sum_f32``            -- the fp32 sum before any epilogue;
 * ``bf16_rne``, ``e4m3_rne_sat``, ``mx_exponent`` -- the scalar conversions.
 
@@ -64,8 +66,11 @@ def _L():
         lib.oracle_combine_residual_rmsnorm.argtypes = (
             common + [P, P, F, F, P, P] + dims)
         lib.oracle_combine_mxfp8.argtypes = common + [P, P] + dims
+        lib.oracle_combine_residual_rmsnorm_mxfp8.argtypes = (
+            common + [P, P, F, F, P, P, P, P] + dims)
         for f in ("oracle_routed_sum_f32", "oracle_combine",
-                  "oracle_combine_residual_rmsnorm", "oracle_combine_mxfp8"):
+                  "oracle_combine_residual_rmsnorm", "oracle_combine_mxfp8",
+                  "oracle_combine_residual_rmsnorm_mxfp8"):
             getattr(lib, f).restype = I
         lib.oracle_bf16_rne.argtypes = [F]
         lib.oracle_bf16_rne.restype = ctypes.c_uint16
@@ -163,6 +168,29 @@ def combine_mxfp8(payload, src_info, weights=None, shared=None, checked=True):
                                   _ptr(shared), _ptr(codes), _ptr(scales), T, H,
                                   k, ep, mtpr, int(checked)))
     return codes, scales
+
+
+def combine_residual_rmsnorm_mxfp8(payload, src_info, weights, shared, residual,
+                                   gamma, eps, weight_bias=0.0, checked=True):
+    """Returns (residual_out bf16 bits, norm_out bf16 bits, codes, scales)."""
+    payload, src_info, weights, shared, (T, H, k, ep, mtpr) = _prep(
+        payload, src_info, weights, shared)
+    if H % 32:
+        raise ValueError("hidden must be a multiple of 32 for MXFP8")
+    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    if residual.shape != (T, H) or gamma.shape != (H,):
+        raise ValueError("residual [T, H] and gamma [H] expected")
+    ro = np.empty((T, H), dtype=np.uint16)
+    no = np.empty((T, H), dtype=np.uint16)
+    codes = np.empty((T, H), dtype=np.uint8)
+    scales = np.empty((T, H // 32), dtype=np.uint8)
+    _rc(_L().oracle_combine_residual_rmsnorm_mxfp8(
+        _ptr(payload), _ptr(src_info), _ptr(weights), _ptr(shared),
+        _ptr(residual), _ptr(gamma), float(eps),
+        float(0.0 if weight_bias is None else weight_bias), _ptr(ro), _ptr(no),
+        _ptr(codes), _ptr(scales), T, H, k, ep, mtpr, int(checked)))
+    return ro, no, codes, scales
 
 
 def bf16_rne(x: float) -> int:

@@ -255,6 +255,67 @@ int oracle_combine_mxfp8(const uint16_t *payload, const int32_t *src_info,
     return 0;
 }
 
+/* Combine + residual add + RMSNorm, with the normalised row quantised to
+ * MXFP8. This composes the two epilogues above: the RMSNorm of
+ * flashinfer.comm.trtllm_moe_allreduce_fusion (Parameters residual_out,
+ * norm_out, weight_bias; its quant_out is a quantised copy of the normalised
+ * output) with the MXFP8 format of flashinfer.comm.moe_a2a_combine
+ * (Parameters output_dtype, output_scales).
+ *   residual_out = bf16_rne(acc + residual_in)                      (as above)
+ *   n_h          = (float)(residual_out_h * rstd * (gamma_h + weight_bias))
+ *   norm_out_h   = bf16_rne(n_h)               (written only if norm_out)
+ *   per block of 32 of n: e = oracle_mx_exponent(amax), scale = e + 127,
+ *   code = e4m3_rne_sat(n_h * 2^-e)            (NaN/inf blocks as above).
+ * The quantiser reads the fp32 values n_h, not their bf16 rounding. */
+int oracle_combine_residual_rmsnorm_mxfp8(
+    const uint16_t *payload, const int32_t *src_info, const float *weights,
+    const uint16_t *shared, const uint16_t *residual_in, const uint16_t *gamma,
+    float eps, float weight_bias, uint16_t *residual_out, uint16_t *norm_out,
+    uint8_t *out_fp8, uint8_t *out_scales, int64_t T, int64_t H, int k, int ep,
+    int64_t mtpr, int checked)
+{
+    if (check_dims(T, H, k, ep, mtpr) || H % 32) return 2;
+    if (checked && check_slots(src_info, T, k, ep, mtpr)) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = routed_sum(payload, src_info, weights, shared, t, h, H,
+                                   k, mtpr);
+            float s = acc + bf16_to_float(residual_in[t * H + h]);
+            uint16_t ro = oracle_bf16_rne(s);
+            residual_out[t * H + h] = ro;
+            double x = (double)bf16_to_float(ro);
+            ss += x * x;
+        }
+        double rstd = 1.0 / sqrt(ss / (double)H + (double)eps);
+        for (int64_t b = 0; b < H / 32; ++b) {
+            float n[32];
+            float amax = 0.0f;
+            int nonfinite = 0;
+            for (int i = 0; i < 32; ++i) {
+                int64_t h = b * 32 + i;
+                double x = (double)bf16_to_float(residual_out[t * H + h]);
+                float g = bf16_to_float(gamma[h]) + weight_bias;
+                n[i] = (float)(x * rstd * (double)g);
+                if (norm_out)
+                    norm_out[t * H + h] = oracle_bf16_rne(n[i]);
+                if (!isfinite(n[i]))
+                    nonfinite = 1;
+                else if (fabsf(n[i]) > amax)
+                    amax = fabsf(n[i]);
+            }
+            int e = nonfinite ? 128 : oracle_mx_exponent(amax);
+            out_scales[t * (H / 32) + b] = (uint8_t)(e + 127);
+            if (e == 128)
+                e = 0;
+            for (int i = 0; i < 32; ++i)
+                out_fp8[t * H + b * 32 + i] = oracle_e4m3_rne_sat(ldexpf(n[i], -e));
+        }
+    }
+    return 0;
+}
+
 /* ---- threading ----------------------------------------------------------- */
 
 void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

@@ -100,8 +100,12 @@ def load_fixture(name):
                                    else [_num(v) for v in b])
         elif hs[0] == "scales":
             fx["scales"][int(hs[1])] = [int(v) for v in body.split()]
+        elif hs[0] == "codes" and cur is not None:
+            cur.setdefault("codes", {})[int(hs[1])] = [int(v, 16) for v in body.split()]
         elif hs[0] == "codes":
             fx["codes"][int(hs[1])] = [int(v, 16) for v in body.split()]
+        elif hs[0] == "scale":
+            cur.setdefault("scale", {})[int(hs[1])] = [int(v) for v in body.split()]
         else:
             raise ValueError(l)
     return fx
@@ -515,3 +519,48 @@ def test_mxfp8_full_pipeline_consistency():
     q = blocks * np.exp2(-e.astype(np.float64))[..., None]
     ref = _brute.nearest_e4m3_vec(q.reshape(-1)).reshape(inp.T, inp.H)
     np.testing.assert_array_equal(codes, ref)
+
+
+# ------------------------------------------- RMSNorm + MXFP8 of the norm
+
+def test_golden_rmsnorm_mxfp8():
+    fx = load_fixture("rmsnorm_mxfp8_small.txt")
+    payload, src, w = build_arrays(fx)
+    res = to_bf16_bits(fx["residual"][0])[None]
+    gamma = to_bf16_bits(fx["gamma"])
+    assert len(fx["cases"]) == 2
+    for case in fx["cases"]:
+        ro, no, codes, scales = oracle.combine_residual_rmsnorm_mxfp8(
+            payload, src, w, None, res, gamma, case["eps"], case["weight_bias"])
+        np.testing.assert_array_equal(ro[0], to_bf16_bits([2, -2] * 16))
+        assert list(scales[0]) == case["scale"][0], case["name"]
+        assert list(codes[0]) == case["codes"][0], case["name"]
+
+
+@pytest.mark.parametrize("wb", [0.0, 1.0])
+def test_rmsnorm_mxfp8_matches_independent_recomputation(wb):
+    """The normalised row recomputed in numpy (exact sum of squares, float64
+    scaling, fp32 rounding) and quantised by code search equals the oracle's
+    codes and scales; residual_out and norm_out equal the RMSNorm oracle's."""
+    inp = _rms_inputs(seed=7, T=16, H=1024, shared_sd=0.5)
+    ro, no, codes, scales = oracle.combine_residual_rmsnorm_mxfp8(
+        inp.payload, inp.src_info, inp.weights, inp.shared, inp.residual,
+        inp.gamma, inp.eps, wb)
+    ro2, no2 = oracle.combine_residual_rmsnorm(
+        inp.payload, inp.src_info, inp.weights, inp.shared, inp.residual,
+        inp.gamma, inp.eps, wb)
+    np.testing.assert_array_equal(ro, ro2)
+    np.testing.assert_array_equal(no, no2)
+    x = bf16_to_f32(ro).astype(np.float64)
+    ss = np.array([math.fsum(r * r) for r in x])
+    rstd = 1.0 / np.sqrt(ss / inp.H + np.float64(np.float32(inp.eps)))
+    g = (bf16_to_f32(inp.gamma) + np.float32(wb)).astype(np.float64)
+    n = (x * rstd[:, None] * g[None, :]).astype(np.float32)
+    np.testing.assert_array_equal(no, to_bf16_bits(n))
+    blocks = n.astype(np.float64).reshape(inp.T, -1, 32)
+    amax = np.abs(blocks).max(axis=2)
+    e = np.array([[-127 if a == 0 else max(-127, _brute.floor_log2(Fraction(float(a))) - 8)
+                   for a in row] for row in amax])
+    np.testing.assert_array_equal(scales, (e + 127).astype(np.uint8))
+    q = blocks * np.exp2(-e.astype(np.float64))[..., None]
+    np.testing.assert_array_equal(codes, _brute.nearest_e4m3_vec(q.reshape(-1)).reshape(inp.T, inp.H))
