@@ -29,13 +29,16 @@ METRIC = "combined tokens/s + achieved HBM GB/s (% peak), T=4096 H=7168 top_k=8"
 PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 
 KIND = {"dsv3": "bf16", "skewed": "bf16", "tiny": "bf16", "rmsnorm": "rmsnorm",
-        "mxfp8": "mxfp8"}
+        "mxfp8": "mxfp8", "rmsnorm_mxfp8": "rmsnorm_mxfp8"}
+# workloads that reuse another workload's inputs
+INPUTS = {"rmsnorm_mxfp8": "rmsnorm"}
 DESCR = {
     "dsv3": "moe combine T=4096 H=7168 top_k=8 E=256 ep=8, bf16 out",
     "skewed": "moe combine T=8192 H=4096 top_k=8 E=128 ep=8 zipf1.2, 10% drops + capacity, shared expert, bf16 out",
     "rmsnorm": "moe combine + residual + RMSNorm T=2048 H=7168 top_k=8 E=256 ep=8, weight_bias=1",
     "mxfp8": "moe combine T=16384 H=7168 top_k=8 E=256 ep=8, MXFP8 e4m3 out + UE8M0/32 scales",
     "tiny": "moe combine T=64 H=1024 top_k=2 E=8 ep=1, bf16 out",
+    "rmsnorm_mxfp8": "moe combine + residual + RMSNorm T=2048 H=7168 top_k=8 E=256 ep=8, weight_bias=1, normalised row as MXFP8 e4m3 + UE8M0/32",
 }
 
 
@@ -91,7 +94,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
-    inp = gen.make_inputs(args.workload, args.seed)
+    inp = gen.make_inputs(INPUTS.get(args.workload, args.workload), args.seed)
     T, H, k, ep, mtpr = inp.T, inp.H, inp.k, inp.ep, inp.mtpr
     algo_bytes = gen.algorithmic_bytes(inp, kind)
 
@@ -101,7 +104,7 @@ def main():
     base = dict(payload=d16(inp.payload), src=torch.from_numpy(inp.src_info).to(dev),
                 w=torch.from_numpy(inp.weights).to(dev),
                 shared=None if inp.shared is None else d16(inp.shared))
-    if kind == "rmsnorm":
+    if kind in ("rmsnorm", "rmsnorm_mxfp8"):
         base["res"] = d16(inp.residual)
         base["gamma"] = d16(inp.gamma)
     per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
@@ -114,6 +117,10 @@ def main():
         elif kind == "rmsnorm":
             s["ro"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             s["no"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        elif kind == "rmsnorm_mxfp8":
+            s["ro"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            s["codes"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
+            s["scales"] = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
         else:
             s["codes"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
             s["scales"] = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
@@ -134,6 +141,11 @@ def main():
             a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["res"]),
                  P(s["gamma"]), inp.eps, 1.0, P(s["ro"]), P(s["no"]), T, H, k, ep, mtpr, sptr)
             calls.append((L.moe_combine_residual_rmsnorm, a))
+        elif kind == "rmsnorm_mxfp8":
+            a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["res"]),
+                 P(s["gamma"]), inp.eps, 1.0, P(s["ro"]), None, P(s["codes"]), P(s["scales"]),
+                 T, H, k, ep, mtpr, sptr)
+            calls.append((L.moe_combine_residual_rmsnorm_mxfp8, a))
         else:
             a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["codes"]),
                  P(s["scales"]), T, H, k, ep, mtpr, sptr)
@@ -209,6 +221,10 @@ def main():
             run = lambda: oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
                                                           inp.shared, inp.residual, inp.gamma,
                                                           inp.eps, 1.0, checked=False)
+        elif kind == "rmsnorm_mxfp8":
+            run = lambda: oracle.combine_residual_rmsnorm_mxfp8(
+                inp.payload, inp.src_info, inp.weights, inp.shared, inp.residual, inp.gamma,
+                inp.eps, 1.0, checked=False)
         else:
             run = lambda: oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights, inp.shared,
                                                checked=False)
@@ -232,7 +248,8 @@ def main():
                    "top_k": k, "ep_size": ep, "max_tokens_per_rank": mtpr,
                    "kept_slots": inp.meta["kept_slots"], "io_dtype": "bf16",
                    "seed": args.seed, "input_sets": nsets,
-                   "launch": mc.describe_launch({"bf16": 0, "rmsnorm": 1, "mxfp8": 2}[kind], T, H, k)},
+                   "launch": mc.describe_launch({"bf16": 0, "rmsnorm": 1, "mxfp8": 2,
+                                                 "rmsnorm_mxfp8": 3}[kind], T, H, k)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": algo_bytes,

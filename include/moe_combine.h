@@ -105,6 +105,9 @@ moe_status_t moe_combine(const void *payload, const int32_t *src_info,
  *   residual_out     = bf16(s)
  *   rstd             = 1 / sqrt(mean_h(residual_out^2) + eps)
  *   norm_out[t, h]   = bf16(residual_out * rstd * (gamma[h] + weight_bias))
+ * rstd and the product are evaluated in fp64 and rounded once to fp32, then
+ * to bf16. Rows of up to 32768 elements are supported (MOE_ERR_UNSUPPORTED
+ * beyond).
  * weight_bias = 0 gives the standard RMSNorm; 1 gives the (1 + gamma) form.
  * residual_in, residual_out and norm_out are [>= num_tokens, hidden] bf16;
  * gamma is [hidden] bf16. residual_out may equal residual_in (in-place
@@ -148,9 +151,33 @@ moe_status_t moe_combine_mxfp8(const void *payload, const int32_t *src_info,
                                int64_t max_tokens_per_rank, void *stream);
 
 /*
+ * Routed combine fused with a residual add, an RMSNorm, and MXFP8
+ * quantisation of the normalised row (the quantised copy that feeds the next
+ * layer's fp8 GEMM).
+ *   residual_out  = bf16(acc + residual_in)                  as above
+ *   n[t, h]       = residual_out * rstd * (gamma[h] + weight_bias)
+ *   norm_out      = bf16(n)          written only if norm_out != NULL
+ *   out_fp8, out_scales = MXFP8 of n, per the rule of moe_combine_mxfp8
+ * The quantiser reads n as fp32, not its bf16 rounding. The RMSNorm
+ * statistic and n are evaluated in fp64 and rounded once to fp32.
+ * residual_out may equal residual_in. No other pair of arguments may
+ * overlap. hidden must be a multiple of 32.
+ * Sources: flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters
+ * residual_out, norm_out, weight_bias and quant_out / scale_out (a quantised
+ * copy of the normalised output); flashinfer.comm.moe_a2a_combine,
+ * Parameters output_dtype (float8_e4m3fn) and output_scales (UE8M0, 32).
+ */
+moe_status_t moe_combine_residual_rmsnorm_mxfp8(
+    const void *payload, const int32_t *src_info, const float *router_weights,
+    const void *shared_out, const void *residual_in, const void *gamma,
+    float eps, float weight_bias, void *residual_out, void *norm_out,
+    void *out_fp8, uint8_t *out_scales, int64_t num_tokens, int32_t hidden,
+    int32_t top_k, int32_t ep_size, int64_t max_tokens_per_rank, void *stream);
+
+/*
  * Describes the launch an entry point would make for these sizes, without
  * touching the GPU. kind: 0 = moe_combine, 1 = residual + RMSNorm,
- * 2 = MXFP8.
+ * 2 = MXFP8, 3 = residual + RMSNorm + MXFP8.
  *
  * On success, writes a NUL-terminated text into buf, such as
  * "threads=128 vec_per_thread=1 chunks=7 blocks=28672 slot_tile=8 masked=0",

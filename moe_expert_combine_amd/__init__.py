@@ -25,6 +25,7 @@ import torch
 from . import _build
 
 __all__ = ["moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
+           "moe_combine_residual_rmsnorm_mxfp8",
            "describe_launch", "abi_version", "lib", "library_path",
            "MoeCombineError"]
 
@@ -52,7 +53,9 @@ def _load():
     L.moe_combine.argtypes = [P, P, P, P, P] + dims
     L.moe_combine_residual_rmsnorm.argtypes = [P, P, P, P, P, P, F, F, P, P] + dims
     L.moe_combine_mxfp8.argtypes = [P, P, P, P, P, P] + dims
-    for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8"):
+    L.moe_combine_residual_rmsnorm_mxfp8.argtypes = [P, P, P, P, P, P, F, F, P, P, P, P] + dims
+    for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
+              "moe_combine_residual_rmsnorm_mxfp8"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_combine_describe_launch.argtypes = [ctypes.c_int, I64, I32, I32, ctypes.c_char_p, I32]
     L.moe_combine_describe_launch.restype = ctypes.c_int
@@ -87,7 +90,8 @@ def abi_version() -> int:
 
 
 def describe_launch(kind: int, num_tokens: int, hidden: int, top_k: int) -> str:
-    """Launch shape an entry point would use (kind 0 bf16, 1 RMSNorm, 2 MXFP8)."""
+    """Launch shape an entry point would use (kind 0 bf16, 1 RMSNorm, 2 MXFP8,
+    3 RMSNorm + MXFP8)."""
     buf = ctypes.create_string_buffer(256)
     _check("moe_combine_describe_launch",
            lib().moe_combine_describe_launch(kind, num_tokens, hidden, top_k, buf, 256))
@@ -198,3 +202,35 @@ def moe_combine_mxfp8(payload, src_info, router_weights=None, shared_out=None,
         _ptr(payload), _ptr(src_info), _ptr(router_weights), _ptr(shared_out),
         _ptr(out_fp8), _ptr(out_scales), T, H, k, ep, mtpr, _stream(dev)))
     return out_fp8, out_scales
+
+
+def moe_combine_residual_rmsnorm_mxfp8(payload, src_info, router_weights, shared_out,
+                                       residual_in, gamma, eps, weight_bias=0.0,
+                                       residual_out=None, out_fp8=None, out_scales=None,
+                                       norm_out=None, want_norm_out=False):
+    """Combine + residual add + RMSNorm, normalised row quantised to MXFP8.
+    Returns (residual_out, out_fp8, out_scales, norm_out); norm_out (bf16) is
+    written only if passed in or ``want_norm_out`` is set, else None."""
+    dev, (T, H, k, ep, mtpr) = _common(payload, src_info, router_weights, shared_out)
+    if H % 32:
+        raise ValueError("hidden must be a multiple of 32 for MXFP8")
+    _need(residual_in, "residual_in", torch.bfloat16, dev, 2)
+    if residual_in.shape[0] < T or residual_in.shape[1] != H:
+        raise ValueError(f"residual_in must be [>= {T}, {H}]")
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    if gamma.shape[0] != H:
+        raise ValueError(f"gamma must be [{H}]")
+    mk = lambda: torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    residual_out = _out(residual_out, "residual_out", torch.bfloat16, dev, T, H, mk)
+    out_fp8 = _out(out_fp8, "out_fp8", torch.float8_e4m3fn, dev, T, H,
+                   lambda: torch.empty((T, H), dtype=torch.float8_e4m3fn, device=dev))
+    out_scales = _out(out_scales, "out_scales", torch.uint8, dev, T, H // 32,
+                      lambda: torch.empty((T, H // 32), dtype=torch.uint8, device=dev))
+    if norm_out is not None or want_norm_out:
+        norm_out = _out(norm_out, "norm_out", torch.bfloat16, dev, T, H, mk)
+    wb = 0.0 if weight_bias is None else float(weight_bias)
+    _check("moe_combine_residual_rmsnorm_mxfp8", lib().moe_combine_residual_rmsnorm_mxfp8(
+        _ptr(payload), _ptr(src_info), _ptr(router_weights), _ptr(shared_out),
+        _ptr(residual_in), _ptr(gamma), float(eps), wb, _ptr(residual_out),
+        _ptr(norm_out), _ptr(out_fp8), _ptr(out_scales), T, H, k, ep, mtpr, _stream(dev)))
+    return residual_out, out_fp8, out_scales, norm_out

@@ -28,7 +28,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-enum Epilogue { EPI_BF16 = 0, EPI_RMSNORM = 1, EPI_MXFP8 = 2 };
+enum Epilogue { EPI_BF16 = 0, EPI_RMSNORM = 1, EPI_MXFP8 = 2, EPI_RMSNORM_MXFP8 = 3 };
 
 struct KernelArgs {
     const uint16_t *payload;   // [ep, mtpr, H] bf16
@@ -38,7 +38,9 @@ struct KernelArgs {
     const uint16_t *residual;  // [T, H]   (RMSNorm)
     const uint16_t *gamma;     // [H]      (RMSNorm)
     void *out0;                // bf16 out | residual_out | e4m3 codes
-    void *out1;                // norm_out | UE8M0 scales
+    void *out1;                // norm_out | UE8M0 scales | e4m3 codes of the norm
+    void *out2;                // UE8M0 scales of the norm (RMSNorm + MXFP8)
+    void *out3;                // bf16 norm_out or null (RMSNorm + MXFP8)
     int64_t mtpr;              // rows per rank
     int32_t H;                 // hidden
     int32_t nvec;              // H / 8
@@ -101,17 +103,55 @@ __device__ __forceinline__ int quad_max(int v) {
     return v;
 }
 
-// Sum over the workgroup; every thread gets the same value (fixed order).
-__device__ __forceinline__ float block_sum(float v, float *lds) {
+// Sum over the workgroup in fp64; every thread gets the same value (butterfly
+// within each wave, then the wave partials in a fixed order from LDS).
+__device__ __forceinline__ double block_sum(double v, double *lds) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     const int wid = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) lds[wid] = v;
     __syncthreads();
     const int nw = (blockDim.x + 63) >> 6;
-    float s = 0.0f;
+    double s = 0.0;
     for (int i = 0; i < nw; ++i) s += lds[i];
     return s;
+}
+
+// MXFP8 quantisation of V vectors of 8 fp32 values held by this lane
+// (flashinfer.comm.moe_a2a_combine, Parameters output_dtype float8_e4m3fn and
+// output_scales UE8M0 with 32 elements per scale). A 32-element block is the
+// 4 vectors of one DPP quad of lanes: amax is a quad max of the integer
+// magnitudes (NaN patterns sort above infinity), the scale byte is the
+// exponent field of amax minus 8, clamped at 0 (floor(log2 amax) - 8 + 127),
+// 0xFF for NaN/inf blocks, and codes are e4m3 of x * 2^-e. Must be reached by
+// every lane of the wave (no divergence around the DPP reads).
+template <int V>
+__device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const bool (&ok)[V],
+                                                  const int (&vi)[V], int64_t row_off,
+                                                  int64_t scale_row_off, uint8_t *codes,
+                                                  uint8_t *scales) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        int m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, (int)(__float_as_uint(x[v][e]) & 0x7FFFFFFFu));
+        m = quad_max(m);
+        const unsigned ef = (unsigned)m >> 23;                  // exponent field of amax
+        const unsigned sbyte = ef == 255u ? 255u : (ef > 8u ? ef - 8u : 0u);
+        // 2^-e as an fp32 bit pattern, e = sbyte - 127 (e = 0 for NaN/inf blocks)
+        const float inv = ef == 255u ? 1.0f : __uint_as_float((254u - sbyte) << 23);
+        if (!ok[v]) continue;
+        u32x2 o = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const unsigned sgn = (__float_as_uint(x[v][e]) >> 24) & 0x80u;
+            const float q = x[v][e] * inv;
+            const unsigned code = sgn | e4m3_mag(__float_as_uint(q) & 0x7FFFFFFFu);
+            o[e >> 2] |= code << ((e & 3) * 8);
+        }
+        st_stream(codes + row_off + (int64_t)vi[v] * 8, o);
+        if ((threadIdx.x & 3) == 0) scales[scale_row_off + (vi[v] >> 2)] = (uint8_t)sbyte;
+    }
 }
 
 // Register budget: KT * V 16-byte loads are in flight per lane (KT * V <= 16,
@@ -125,7 +165,7 @@ constexpr int max_threads_for() { return V >= 4 ? 512 : 1024; }
 // chunk may run past hidden / 8 vectors; SH: a shared-expert row is added.
 template <int KT, int V, int EPI, bool MASK, bool SH>
 __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArgs a) {
-    __shared__ float lds_red[16];
+    __shared__ double lds_red[16];
     const int nt = blockDim.x;
     const int tid = threadIdx.x;
     const int t = blockIdx.x / a.chunks;
@@ -154,7 +194,7 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
         shv[v] = resv[v] = gmv[v] = (u32x4){0u, 0u, 0u, 0u};
         if (!ok[v]) continue;
         if constexpr (SH) shv[v] = ld_stream(a.shared + row_off + (int64_t)vi[v] * 8);
-        if constexpr (EPI == EPI_RMSNORM) {
+        if constexpr (EPI == EPI_RMSNORM || EPI == EPI_RMSNORM_MXFP8) {
             resv[v] = ld_stream(a.residual + row_off + (int64_t)vi[v] * 8);
             if constexpr (V <= 4) gmv[v] = ld_cached(a.gamma + (int64_t)vi[v] * 8);
         }
@@ -238,12 +278,15 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
             for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[v][2 * i], acc[v][2 * i + 1]);
             st_stream(out + row_off + (int64_t)vi[v] * 8, o);
         }
-    } else if constexpr (EPI == EPI_RMSNORM) {
+    } else if constexpr (EPI == EPI_RMSNORM || EPI == EPI_RMSNORM_MXFP8) {
         // flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters residual_in,
-        // residual_out, rms_gamma, rms_eps, norm_out, weight_bias.
+        // residual_out, rms_gamma, rms_eps, norm_out, weight_bias:
+        //   residual_out = bf16(acc + residual_in)                   (fp32 add)
+        //   n = residual_out * rstd * (gamma + weight_bias)
+        // The statistic and the scaling are done in fp64 (each x^2 of a bf16
+        // value is exact), so n matches a double-precision evaluation.
         uint16_t *res_out = static_cast<uint16_t *>(a.out0);
-        uint16_t *norm_out = static_cast<uint16_t *>(a.out1);
-        float ss = 0.0f;
+        double ss = 0.0;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             if (!ok[v]) continue;
@@ -258,58 +301,40 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
             for (int e = 0; e < 8; ++e) {
                 const float xr = bf16_elem(o, e);     // the stored residual
                 acc[v][e] = xr;
-                ss = __builtin_fmaf(xr, xr, ss);
+                ss = __builtin_fma((double)xr, (double)xr, ss);
             }
             st_stream(res_out + row_off + (int64_t)vi[v] * 8, o);
         }
-        const float tot = block_sum(ss, lds_red);
-        const float rstd = 1.0f / __builtin_sqrtf(tot / (float)a.H + a.eps);
+        const double tot = block_sum(ss, lds_red);
+        const double rstd = 1.0 / __builtin_sqrt(tot / (double)a.H + (double)a.eps);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            if (!ok[v]) continue;
             // the widest rows re-read gamma here (L2-resident) to save registers
-            const u32x4 gm = (V <= 4) ? gmv[v] : ld_cached(a.gamma + (int64_t)vi[v] * 8);
-            u32x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float g0 = bf16_elem(gm, 2 * i) + a.wb;
-                const float g1 = bf16_elem(gm, 2 * i + 1) + a.wb;
-                o[i] = pack_bf16x2((acc[v][2 * i] * rstd) * g0,
-                                   (acc[v][2 * i + 1] * rstd) * g1);
-            }
-            st_stream(norm_out + row_off + (int64_t)vi[v] * 8, o);
-        }
-    } else {
-        // flashinfer.comm.moe_a2a_combine, Parameters output_dtype
-        // (float8_e4m3fn) and output_scales (UE8M0, 32 elements per scale).
-        // A 32-element block is the 4 vectors of one DPP quad of lanes.
-        uint8_t *codes = static_cast<uint8_t *>(a.out0);
-        uint8_t *scales = static_cast<uint8_t *>(a.out1);
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            int m = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                m = max(m, (int)(__float_as_uint(acc[v][e]) & 0x7FFFFFFFu));
-            m = quad_max(m);                            // all lanes active here
-            const unsigned ef = (unsigned)m >> 23;      // exponent field of amax
-            // scale byte = clamp(floor(log2 amax) - 8, -127, 127) + 127
-            const unsigned sbyte = ef == 255u ? 255u : (ef > 8u ? ef - 8u : 0u);
-            // 2^-e as an fp32 bit pattern, e = sbyte - 127 (e = 0 for NaN/inf)
-            const float inv = ef == 255u ? 1.0f : __uint_as_float((254u - sbyte) << 23);
-            if (!ok[v]) continue;
-            u32x2 o = {0u, 0u};
+            const u32x4 gm = (V <= 4) ? gmv[v] : (ok[v] ? ld_cached(a.gamma + (int64_t)vi[v] * 8)
+                                                       : (u32x4){0u, 0u, 0u, 0u});
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const unsigned sgn = (__float_as_uint(acc[v][e]) >> 24) & 0x80u;
-                const float q = acc[v][e] * inv;
-                const unsigned code = sgn | e4m3_mag(__float_as_uint(q) & 0x7FFFFFFFu);
-                o[e >> 2] |= code << ((e & 3) * 8);
+                const float g = bf16_elem(gm, e) + a.wb;
+                acc[v][e] = (float)((double)acc[v][e] * rstd * (double)g);
             }
-            st_stream(codes + row_off + (int64_t)vi[v] * 8, o);
-            if ((tid & 3) == 0)
-                scales[(int64_t)t * (a.H >> 5) + (vi[v] >> 2)] = (uint8_t)sbyte;
         }
+        uint16_t *norm_out = static_cast<uint16_t *>(EPI == EPI_RMSNORM ? a.out1 : a.out3);
+        if (norm_out) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (!ok[v]) continue;
+                u32x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[v][2 * i], acc[v][2 * i + 1]);
+                st_stream(norm_out + row_off + (int64_t)vi[v] * 8, o);
+            }
+        }
+        if constexpr (EPI == EPI_RMSNORM_MXFP8)
+            mx_quantize_store<V>(acc, ok, vi, row_off, (int64_t)t * (a.H >> 5),
+                                 static_cast<uint8_t *>(a.out1), static_cast<uint8_t *>(a.out2));
+    } else {
+        mx_quantize_store<V>(acc, ok, vi, row_off, (int64_t)t * (a.H >> 5),
+                             static_cast<uint8_t *>(a.out0), static_cast<uint8_t *>(a.out1));
     }
 }
 

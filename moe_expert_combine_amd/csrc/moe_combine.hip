@@ -67,7 +67,7 @@ moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
     p->kt = k <= 2 ? 2 : (k <= 4 ? 4 : 8);
     int threads = 0, vec = 0;
     const bool forced = tile_override(&threads, &vec);
-    if (kind == moe::EPI_RMSNORM) {
+    if (kind == moe::EPI_RMSNORM || kind == moe::EPI_RMSNORM_MXFP8) {
         // The row reduction needs the whole token in one workgroup.
         if (!forced) {
             vec = 0;
@@ -268,14 +268,56 @@ moe_status_t moe_combine_mxfp8(const void *payload, const int32_t *src_info, con
     return launch<moe::EPI_MXFP8>(p, a, stream);
 }
 
+moe_status_t moe_combine_residual_rmsnorm_mxfp8(const void *payload, const int32_t *src_info,
+                                                const float *router_weights, const void *shared_out,
+                                                const void *residual_in, const void *gamma, float eps,
+                                                float weight_bias, void *residual_out, void *norm_out,
+                                                void *out_fp8, uint8_t *out_scales, int64_t num_tokens,
+                                                int32_t hidden, int32_t top_k, int32_t ep_size,
+                                                int64_t max_tokens_per_rank, void *stream) {
+    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
+                                   ep_size, max_tokens_per_rank);
+    if (st != MOE_OK) return st;
+    if (hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8 (got %d)", hidden);
+    Plan p;
+    if ((st = make_plan(moe::EPI_RMSNORM_MXFP8, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    if (num_tokens == 0) return ok();
+    if (!residual_in || !gamma || !residual_out || !out_fp8 || !out_scales)
+        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out, out_fp8 and out_scales are required");
+    if (!aligned(residual_in, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) ||
+        (norm_out && !aligned(norm_out, 16)) || !aligned(out_fp8, 8))
+        return fail(MOE_ERR_INVALID_ARG, "misaligned residual_in, gamma, residual_out, norm_out or out_fp8");
+    const void *outs[4] = {residual_out, norm_out, out_fp8, out_scales};
+    for (int i = 0; i < 4; ++i) {
+        if (!outs[i]) continue;
+        if (outs[i] == payload || outs[i] == shared_out || outs[i] == gamma)
+            return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input");
+        if (i > 0 && outs[i] == residual_in) return fail(MOE_ERR_INVALID_ARG, "only residual_out may alias residual_in");
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return fail(MOE_ERR_INVALID_ARG, "outputs must not alias each other");
+    }
+    if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    a.residual = static_cast<const uint16_t *>(residual_in);
+    a.gamma = static_cast<const uint16_t *>(gamma);
+    a.out0 = residual_out;
+    a.out1 = out_fp8;
+    a.out2 = out_scales;
+    a.out3 = norm_out;
+    a.eps = eps;
+    a.wb = weight_bias;
+    return launch<moe::EPI_RMSNORM_MXFP8>(p, a, stream);
+}
+
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,
                                          int32_t buflen) {
-    if (kind < 0 || kind > 2) return fail(MOE_ERR_INVALID_ARG, "kind must be 0, 1 or 2");
+    if (kind < 0 || kind > 3) return fail(MOE_ERR_INVALID_ARG, "kind must be 0, 1, 2 or 3");
     if (!buf || buflen < 1) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or empty");
     moe_status_t st = check_common(reinterpret_cast<const void *>(16), reinterpret_cast<const int32_t *>(16), nullptr,
                                    nullptr, num_tokens, hidden, top_k, 1, 1);
     if (st != MOE_OK) return st;
-    if (kind == 2 && hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8");
+    if ((kind == 2 || kind == 3) && hidden % 32)
+        return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8");
     Plan p;
     if ((st = make_plan(kind, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
     snprintf(buf, (size_t)buflen, "threads=%d vec_per_thread=%d chunks=%d blocks=%lld slot_tile=%d masked=%d",

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
-              "moe_combine_describe_launch", "moe_combine_abi_version",
+              "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_describe_launch", "moe_combine_abi_version",
               "moe_combine_status_string", "moe_combine_last_error"):
         assert n in names
 
@@ -110,6 +110,26 @@ def test_mxfp8_argument_errors():
     assert f(s=5 * A) == INVALID                 # scales alias codes
 
 
+def test_rmsnorm_mxfp8_argument_errors():
+    L = mc.lib()
+
+    def f(ro=5 * A, no=None, o=6 * A, sc=7 * A, H=64, res=3 * A, g=4 * A, eps=1e-6):
+        return L.moe_combine_residual_rmsnorm_mxfp8(A, A, A, None, res, g, eps, 1.0, ro, no,
+                                                     o, sc, 4, H, 2, 1, 8, None)
+    assert f(H=40) == INVALID                 # not a multiple of 32
+    assert f(ro=None) == INVALID
+    assert f(o=None) == INVALID
+    assert f(sc=None) == INVALID
+    assert f(g=None) == INVALID
+    assert f(no=6 * A) == INVALID             # norm_out aliases out_fp8
+    assert f(o=3 * A) == INVALID              # out_fp8 aliases residual_in
+    assert f(sc=5 * A) == INVALID             # scales alias residual_out
+    assert f(o=6 * A + 4) == INVALID          # misaligned codes
+    assert f(eps=-1.0) == INVALID
+    assert L.moe_combine_residual_rmsnorm_mxfp8(None, None, None, None, None, None, 1e-6, 0.0,
+                                                None, None, None, None, 0, 64, 2, 1, 8, None) == OK
+
+
 def test_describe_launch_shapes():
     d = mc.describe_launch(0, 4096, 7168, 8)
     assert "threads=64 vec_per_thread=2 chunks=7 blocks=28672 slot_tile=8 masked=0" == d
@@ -117,6 +137,9 @@ def test_describe_launch_shapes():
     assert "chunks=4" in d and "masked=0" in d
     d = mc.describe_launch(1, 2048, 7168, 8)
     assert "threads=448 vec_per_thread=2 chunks=1" in d
+    assert d == mc.describe_launch(3, 2048, 7168, 8)
+    with pytest.raises(mc.MoeCombineError):
+        mc.describe_launch(3, 4, 48, 2)
     d = mc.describe_launch(2, 16384, 7168, 8)
     assert "masked=0" in d
     d = mc.describe_launch(0, 5, 264, 3)          # ragged: 33 vectors
