@@ -15,8 +15,11 @@ the documentation pages it follows, is stated in ``oracle.c``:
 * ``combine_mxfp8``             -- + MXFP8 e4m3 codes and UE8M0 scales / 32;
 * ``combine_residual_rmsnorm_mxfp8`` -- RMSNorm whose normalised row is also
                                    quantised to MXFP8;
+* ``combine_mxfp4``             -- + MXFP4 e2m1 codes (two per byte) and
+                                   UE8M0 scales / 32;
 * ``routed_sum_f32``            -- the fp32 sum before any epilogue;
-* ``bf16_rne``, ``e4m3_rne_sat``, ``mx_exponent`` -- the scalar conversions.
+* ``bf16_rne``, ``e4m3_rne_sat``, ``mx_exponent``, ``e2m1_rne_sat``,
+  ``mx4_exponent`` -- the scalar conversions.
 
 Inputs are numpy arrays: bf16 tensors as uint16 bit patterns, ``src_info``
 int32 [T, k, 2] (rank, row) with rank < 0 = dropped slot, ``weights`` float32
@@ -68,9 +71,10 @@ def _L():
         lib.oracle_combine_mxfp8.argtypes = common + [P, P] + dims
         lib.oracle_combine_residual_rmsnorm_mxfp8.argtypes = (
             common + [P, P, F, F, P, P, P, P] + dims)
+        lib.oracle_combine_mxfp4.argtypes = common + [P, P] + dims
         for f in ("oracle_routed_sum_f32", "oracle_combine",
                   "oracle_combine_residual_rmsnorm", "oracle_combine_mxfp8",
-                  "oracle_combine_residual_rmsnorm_mxfp8"):
+                  "oracle_combine_residual_rmsnorm_mxfp8", "oracle_combine_mxfp4"):
             getattr(lib, f).restype = I
         lib.oracle_bf16_rne.argtypes = [F]
         lib.oracle_bf16_rne.restype = ctypes.c_uint16
@@ -78,6 +82,10 @@ def _L():
         lib.oracle_e4m3_rne_sat.restype = ctypes.c_uint8
         lib.oracle_mx_exponent.argtypes = [F]
         lib.oracle_mx_exponent.restype = I
+        lib.oracle_mx4_exponent.argtypes = [F]
+        lib.oracle_mx4_exponent.restype = I
+        lib.oracle_e2m1_rne_sat.argtypes = [F]
+        lib.oracle_e2m1_rne_sat.restype = ctypes.c_uint8
         lib.oracle_set_num_threads.argtypes = [I]
         lib.oracle_set_num_threads.restype = None
         lib.oracle_max_threads.argtypes = []
@@ -191,6 +199,28 @@ def combine_residual_rmsnorm_mxfp8(payload, src_info, weights, shared, residual,
         float(0.0 if weight_bias is None else weight_bias), _ptr(ro), _ptr(no),
         _ptr(codes), _ptr(scales), T, H, k, ep, mtpr, int(checked)))
     return ro, no, codes, scales
+
+
+def combine_mxfp4(payload, src_info, weights=None, shared=None, checked=True):
+    """Returns (packed e2m1 codes uint8 [T, H/2], UE8M0 scales uint8 [T, H/32])."""
+    payload, src_info, weights, shared, (T, H, k, ep, mtpr) = _prep(
+        payload, src_info, weights, shared)
+    if H % 32:
+        raise ValueError("hidden must be a multiple of 32 for MXFP4")
+    codes = np.empty((T, H // 2), dtype=np.uint8)
+    scales = np.empty((T, H // 32), dtype=np.uint8)
+    _rc(_L().oracle_combine_mxfp4(_ptr(payload), _ptr(src_info), _ptr(weights),
+                                  _ptr(shared), _ptr(codes), _ptr(scales), T, H,
+                                  k, ep, mtpr, int(checked)))
+    return codes, scales
+
+
+def e2m1_rne_sat(x: float) -> int:
+    return int(_L().oracle_e2m1_rne_sat(float(x)))
+
+
+def mx4_exponent(amax: float) -> int:
+    return int(_L().oracle_mx4_exponent(float(amax)))
 
 
 def bf16_rne(x: float) -> int:

@@ -108,6 +108,47 @@ uint8_t oracle_e4m3_rne_sat(float q)
     return (uint8_t)(s | (uint8_t)code);
 }
 
+/* Shared exponent of one 32-element MXFP4 block: floor(log2(amax)) - 2,
+ * where 2 is the exponent of e2m1's largest value (6 = 1.5 * 2^2), clamped to
+ * [-127, 127]; amax == 0 gives -127; NaN/inf amax gives 128 (byte 0xFF). */
+int oracle_mx4_exponent(float amax)
+{
+    if (isnan(amax) || isinf(amax))
+        return 128;
+    if (amax == 0.0f)
+        return -127;
+    int ex;
+    (void)frexp((double)amax, &ex);
+    int e = (ex - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* fp32 -> float4 e2m1 code (4 bits: sign, 2 exponent bits with bias 1, 1
+ * mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinity or NaN):
+ * round to nearest even on that grid, saturating at 6. e2m1 has no NaN, so
+ * NaN and infinity both saturate (a block holding them has the NaN scale). */
+uint8_t oracle_e2m1_rne_sat(float q)
+{
+    uint32_t u;
+    memcpy(&u, &q, sizeof u);
+    uint8_t s = (uint8_t)((u >> 28) & 0x8u);
+    if (isnan(q))
+        return (uint8_t)(s | 0x7);
+    double a = fabs((double)q);
+    if (a >= 6.0)
+        return (uint8_t)(s | 0x7);
+    if (a < 1.0)                      /* subnormal step 0.5: codes 0, 1, 2 */
+        return (uint8_t)(s | (uint8_t)rint(a * 2.0));
+    int ex;
+    (void)frexp(a, &ex);
+    int E = ex - 1;                   /* 0, 1 or 2 */
+    double n = rint(ldexp(a, 1 - E)); /* 2..4, ties to even */
+    int code = ((E + 1) << 1) + (int)n - 2;
+    return (uint8_t)(s | (uint8_t)code);
+}
+
 /* ---- the routed sum ----------------------------------------------------- */
 
 static int check_dims(int64_t T, int64_t H, int k, int ep, int64_t mtpr)
@@ -311,6 +352,48 @@ int oracle_combine_residual_rmsnorm_mxfp8(
                 e = 0;
             for (int i = 0; i < 32; ++i)
                 out_fp8[t * H + b * 32 + i] = oracle_e4m3_rne_sat(ldexpf(n[i], -e));
+        }
+    }
+    return 0;
+}
+
+/* Combine with an MXFP4 output (flashinfer.comm.moe_a2a_combine, Parameters
+ * output_scales: UE8M0 scales with vector size 32; output_scalar_scale: the
+ * per-tensor scale is ignored by the MXFP4 path). For each block of 32 fp32
+ * sums, e = oracle_mx4_exponent(amax), scale byte = e + 127, code =
+ * e2m1_rne_sat(acc * 2^-e); two codes per byte, element 2i in the low nibble.
+ * out_fp4 is [T, H/2] bytes, scales [T, H/32] row-major. A block with a NaN or
+ * infinite element gets scale 0xFF and its codes are taken with e = 0. */
+int oracle_combine_mxfp4(const uint16_t *payload, const int32_t *src_info,
+                         const float *weights, const uint16_t *shared,
+                         uint8_t *out_fp4, uint8_t *out_scales, int64_t T,
+                         int64_t H, int k, int ep, int64_t mtpr, int checked)
+{
+    if (check_dims(T, H, k, ep, mtpr) || H % 32) return 2;
+    if (checked && check_slots(src_info, T, k, ep, mtpr)) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b < H / 32; ++b) {
+            float acc[32];
+            float amax = 0.0f;
+            int nonfinite = 0;
+            for (int i = 0; i < 32; ++i) {
+                acc[i] = routed_sum(payload, src_info, weights, shared, t,
+                                    b * 32 + i, H, k, mtpr);
+                if (!isfinite(acc[i]))
+                    nonfinite = 1;
+                else if (fabsf(acc[i]) > amax)
+                    amax = fabsf(acc[i]);
+            }
+            int e = nonfinite ? 128 : oracle_mx4_exponent(amax);
+            out_scales[t * (H / 32) + b] = (uint8_t)(e + 127);
+            if (e == 128)
+                e = 0;
+            for (int i = 0; i < 32; i += 2) {
+                uint8_t lo = oracle_e2m1_rne_sat(ldexpf(acc[i], -e));
+                uint8_t hi = oracle_e2m1_rne_sat(ldexpf(acc[i + 1], -e));
+                out_fp4[t * (H / 2) + (b * 32 + i) / 2] = (uint8_t)(lo | (hi << 4));
+            }
         }
     }
     return 0;

@@ -564,3 +564,89 @@ def test_rmsnorm_mxfp8_matches_independent_recomputation(wb):
     np.testing.assert_array_equal(scales, (e + 127).astype(np.uint8))
     q = blocks * np.exp2(-e.astype(np.float64))[..., None]
     np.testing.assert_array_equal(codes, _brute.nearest_e4m3_vec(q.reshape(-1)).reshape(inp.T, inp.H))
+
+
+# --------------------------------------------------------------- MXFP4
+
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def nearest_e2m1(q):
+    """Nearest e2m1 code by search over the 8 magnitudes (ties -> even code,
+    saturating at 6), sign from q."""
+    a = min(abs(Fraction(q)), Fraction(100)) if math.isfinite(q) else Fraction(100)
+    best, bd = None, None
+    for c, v in enumerate(E2M1_VALUES):
+        d = abs(a - Fraction(v))
+        if bd is None or d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    return best | (0x8 if math.copysign(1.0, q) < 0 else 0)
+
+
+def test_golden_mxfp4():
+    fx = load_fixture("mxfp4_small.txt")
+    d = fx["dims"]
+    x0 = np.array(fx["x"][0], dtype=np.float32)
+    payload = to_bf16_bits(x0)[None, None]
+    np.testing.assert_array_equal(bf16_to_f32(payload[0, 0]), x0)
+    _, src, w = build_arrays({"dims": d, "rows": {}, "slots": fx["slots"]})
+    codes, scales = oracle.combine_mxfp4(payload, src, w)
+    assert list(scales[0]) == fx["scales"][0]
+    assert list(codes[0]) == fx["codes"][0]
+
+
+def test_e2m1_exhaustive_over_bf16_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    q = (bits << 16).view(np.float32)
+    vals = np.array(E2M1_VALUES)
+    fin = q[np.isfinite(q)].astype(np.float64)
+    a = np.minimum(np.abs(fin), 100.0)
+    dist = np.abs(a[:, None] - vals[None, :])
+    dmin = dist.min(axis=1, keepdims=True)
+    tie = dist == dmin
+    even = tie & (np.arange(8)[None, :] % 2 == 0)
+    ref = np.where(even.any(axis=1), even.argmax(axis=1), tie.argmax(axis=1))
+    ref = ref | np.where(np.signbit(fin), 8, 0)
+    got = np.array([oracle.e2m1_rne_sat(float(v)) for v in fin])
+    np.testing.assert_array_equal(got, ref)
+    for v in q[~np.isfinite(q)][:50]:
+        assert oracle.e2m1_rne_sat(float(v)) & 0x7 == 0x7
+    for v in [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.3, 5.9, -7.0, 1e30]:
+        assert oracle.e2m1_rne_sat(v) == nearest_e2m1(v), v
+
+
+def test_mx4_exponent_closed_form():
+    rng = np.random.default_rng(9)
+    for a in np.concatenate([2.0 ** np.arange(-149, 128),
+                             rng.random(500) * 10.0 ** rng.integers(-44, 38, 500)]).astype(np.float32):
+        a = float(a)
+        if a == 0:
+            continue
+        e = _brute.floor_log2(Fraction(a)) - 2
+        assert oracle.mx4_exponent(a) == max(-127, min(127, e)), a
+    assert oracle.mx4_exponent(0.0) == -127
+    assert oracle.mx4_exponent(float("nan")) == 128
+
+
+def test_mxfp4_blocks_brute_force():
+    """Tiny shapes: scales and packed codes from the exact-rational routed sum
+    by search, plus the e2m1 error bound and block invariants."""
+    inp = gen.make_inputs(dict(T=5, H=64, E=8, ep=2, k=3, hot_row_frac=0.2,
+                               hot_scale=64.0, shared_sd=0.5), seed=8)
+    pf = bf16_to_f32(inp.payload)
+    acc = np.array(_brute.brute_routed_sum(pf, inp.src_info, inp.weights,
+                                           bf16_to_f32(inp.shared)), np.float64)
+    codes, scales = oracle.combine_mxfp4(inp.payload, inp.src_info, inp.weights, inp.shared)
+    for t in range(inp.T):
+        for b in range(inp.H // 32):
+            blk = acc[t, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            e = -127 if amax == 0 else max(-127, _brute.floor_log2(Fraction(amax)) - 2)
+            assert scales[t, b] == e + 127
+            if amax > 0 and e > -127:
+                assert 4 <= amax * 2.0 ** -e < 8
+            for i in range(32):
+                byte = int(codes[t, (32 * b + i) // 2])
+                c = (byte >> 4) if i % 2 else (byte & 0xF)
+                q = blk[i] * 2.0 ** -e
+                assert c == nearest_e2m1(q), (t, b, i, q)
