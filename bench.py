@@ -29,15 +29,16 @@ METRIC = "combined tokens/s + achieved HBM GB/s (% peak), T=4096 H=7168 top_k=8"
 PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 
 KIND = {"dsv3": "bf16", "skewed": "bf16", "tiny": "bf16", "rmsnorm": "rmsnorm",
-        "mxfp8": "mxfp8", "rmsnorm_mxfp8": "rmsnorm_mxfp8"}
+        "mxfp8": "mxfp8", "rmsnorm_mxfp8": "rmsnorm_mxfp8", "mxfp4": "mxfp4"}
 # workloads that reuse another workload's inputs
-INPUTS = {"rmsnorm_mxfp8": "rmsnorm"}
+INPUTS = {"rmsnorm_mxfp8": "rmsnorm", "mxfp4": "mxfp8"}
 DESCR = {
     "dsv3": "moe combine T=4096 H=7168 top_k=8 E=256 ep=8, bf16 out",
     "skewed": "moe combine T=8192 H=4096 top_k=8 E=128 ep=8 zipf1.2, 10% drops + capacity, shared expert, bf16 out",
     "rmsnorm": "moe combine + residual + RMSNorm T=2048 H=7168 top_k=8 E=256 ep=8, weight_bias=1",
     "mxfp8": "moe combine T=16384 H=7168 top_k=8 E=256 ep=8, MXFP8 e4m3 out + UE8M0/32 scales",
     "tiny": "moe combine T=64 H=1024 top_k=2 E=8 ep=1, bf16 out",
+    "mxfp4": "moe combine T=16384 H=7168 top_k=8 E=256 ep=8, MXFP4 e2m1 out + UE8M0/32 scales",
     "rmsnorm_mxfp8": "moe combine + residual + RMSNorm T=2048 H=7168 top_k=8 E=256 ep=8, weight_bias=1, normalised row as MXFP8 e4m3 + UE8M0/32",
 }
 
@@ -117,6 +118,9 @@ def main():
         elif kind == "rmsnorm":
             s["ro"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             s["no"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        elif kind == "mxfp4":
+            s["codes"] = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+            s["scales"] = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
         elif kind == "rmsnorm_mxfp8":
             s["ro"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             s["codes"] = torch.empty((T, H), dtype=torch.uint8, device=dev)
@@ -146,6 +150,10 @@ def main():
                  P(s["gamma"]), inp.eps, 1.0, P(s["ro"]), None, P(s["codes"]), P(s["scales"]),
                  T, H, k, ep, mtpr, sptr)
             calls.append((L.moe_combine_residual_rmsnorm_mxfp8, a))
+        elif kind == "mxfp4":
+            a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["codes"]),
+                 P(s["scales"]), T, H, k, ep, mtpr, sptr)
+            calls.append((L.moe_combine_mxfp4, a))
         else:
             a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["codes"]),
                  P(s["scales"]), T, H, k, ep, mtpr, sptr)
@@ -221,6 +229,9 @@ def main():
             run = lambda: oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
                                                           inp.shared, inp.residual, inp.gamma,
                                                           inp.eps, 1.0, checked=False)
+        elif kind == "mxfp4":
+            run = lambda: oracle.combine_mxfp4(inp.payload, inp.src_info, inp.weights, inp.shared,
+                                               checked=False)
         elif kind == "rmsnorm_mxfp8":
             run = lambda: oracle.combine_residual_rmsnorm_mxfp8(
                 inp.payload, inp.src_info, inp.weights, inp.shared, inp.residual, inp.gamma,
@@ -249,7 +260,7 @@ def main():
                    "kept_slots": inp.meta["kept_slots"], "io_dtype": "bf16",
                    "seed": args.seed, "input_sets": nsets,
                    "launch": mc.describe_launch({"bf16": 0, "rmsnorm": 1, "mxfp8": 2,
-                                                 "rmsnorm_mxfp8": 3}[kind], T, H, k)},
+                                                 "rmsnorm_mxfp8": 3, "mxfp4": 4}[kind], T, H, k)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": algo_bytes,

@@ -316,7 +316,7 @@ def algorithmic_bytes(inp: Inputs, kind: str = "bf16") -> int:
     """Bytes the combine must move (no padding, no dropped rows): gathered
     valid rows, 12 B of slot map + weight per (token, slot), optional shared,
     residual and gamma reads, and the outputs of ``kind``
-    ("bf16" | "rmsnorm" | "mxfp8" | "rmsnorm_mxfp8")."""
+    ("bf16" | "rmsnorm" | "mxfp8" | "rmsnorm_mxfp8" | "mxfp4")."""
     T, H, k = inp.T, inp.H, inp.k
     b = inp.meta["kept_slots"] * 2 * H + T * k * (8 + (4 if inp.weights is not None else 0))
     if inp.shared is not None:
@@ -327,6 +327,8 @@ def algorithmic_bytes(inp: Inputs, kind: str = "bf16") -> int:
         b += T * H * 2 + H * 2 + 2 * T * H * 2
     elif kind == "mxfp8":
         b += T * H + T * (H // 32)
+    elif kind == "mxfp4":
+        b += T * H // 2 + T * (H // 32)
     elif kind == "rmsnorm_mxfp8":
         # residual in, gamma, residual_out, e4m3 codes and scales of the norm
         b += T * H * 2 + H * 2 + T * H * 2 + T * H + T * (H // 32)

@@ -11,9 +11,13 @@
  *   acc += shared_out[t, h]                   -- only if shared_out != NULL
  *
  * The sum is accumulated in fp32 in that fixed order. It is followed by one
- * of three epilogues: a bf16 store (moe_combine), residual add plus RMSNorm
- * (moe_combine_residual_rmsnorm), or MXFP8 quantisation
- * (moe_combine_mxfp8).
+ * of five epilogues:
+ *  - a bf16 store (moe_combine);
+ *  - residual add plus RMSNorm (moe_combine_residual_rmsnorm);
+ *  - MXFP8 quantisation (moe_combine_mxfp8);
+ *  - residual add, RMSNorm and MXFP8 of the normalised row
+ *    (moe_combine_residual_rmsnorm_mxfp8);
+ *  - MXFP4 quantisation (moe_combine_mxfp4).
  *
  * Sources (documentation pages):
  *  - flashinfer.comm.moe_a2a_combine, Parameters: payload, output_dtype,
@@ -175,9 +179,37 @@ moe_status_t moe_combine_residual_rmsnorm_mxfp8(
     int32_t top_k, int32_t ep_size, int64_t max_tokens_per_rank, void *stream);
 
 /*
+ * Routed combine with an MXFP4 output: float4 e2m1 codes (two per byte)
+ * plus one UE8M0 scale byte per 32 consecutive elements.
+ *
+ * e2m1 has a sign, 2 exponent bits (bias 1) and 1 mantissa bit, with
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, and no inf or NaN. For each block
+ * of 32 sums:
+ *   e     = clamp(floor(log2(amax)) - 2, -127, 127), e = -127 if amax == 0
+ *   scale = e + 127                     (0xFF if the block holds NaN or inf)
+ *   code  = e2m1(acc * 2^-e), rounded to nearest even, saturated at +-6
+ * Here 2 is the exponent of e2m1's largest value, 6 = 1.5 * 2^2. A NaN or
+ * inf block has its codes taken with e = 0, and NaN and inf saturate.
+ *
+ * Layout: out_fp4 is [>= num_tokens, hidden / 2] bytes (4-byte aligned).
+ * Element 2i of a row sits in the low nibble of byte i and element 2i+1 in
+ * the high nibble. out_scales is [>= num_tokens, hidden / 32] uint8,
+ * row-major. hidden must be a multiple of 32.
+ *
+ * Source: flashinfer.comm.moe_a2a_combine, Parameters output_scales (UE8M0,
+ * vector size 32) and output_scalar_scale (ignored by the MXFP4 path).
+ */
+moe_status_t moe_combine_mxfp4(const void *payload, const int32_t *src_info,
+                               const float *router_weights,
+                               const void *shared_out, void *out_fp4,
+                               uint8_t *out_scales, int64_t num_tokens,
+                               int32_t hidden, int32_t top_k, int32_t ep_size,
+                               int64_t max_tokens_per_rank, void *stream);
+
+/*
  * Describes the launch an entry point would make for these sizes, without
  * touching the GPU. kind: 0 = moe_combine, 1 = residual + RMSNorm,
- * 2 = MXFP8, 3 = residual + RMSNorm + MXFP8.
+ * 2 = MXFP8, 3 = residual + RMSNorm + MXFP8, 4 = MXFP4.
  *
  * On success, writes a NUL-terminated text into buf, such as
  * "threads=128 vec_per_thread=1 chunks=7 blocks=28672 slot_tile=8 masked=0",

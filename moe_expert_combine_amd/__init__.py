@@ -25,7 +25,7 @@ import torch
 from . import _build
 
 __all__ = ["moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
-           "moe_combine_residual_rmsnorm_mxfp8",
+           "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
            "describe_launch", "abi_version", "lib", "library_path",
            "MoeCombineError"]
 
@@ -54,8 +54,9 @@ def _load():
     L.moe_combine_residual_rmsnorm.argtypes = [P, P, P, P, P, P, F, F, P, P] + dims
     L.moe_combine_mxfp8.argtypes = [P, P, P, P, P, P] + dims
     L.moe_combine_residual_rmsnorm_mxfp8.argtypes = [P, P, P, P, P, P, F, F, P, P, P, P] + dims
+    L.moe_combine_mxfp4.argtypes = [P, P, P, P, P, P] + dims
     for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
-              "moe_combine_residual_rmsnorm_mxfp8"):
+              "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4"):
         getattr(L, f).restype = ctypes.c_int
     L.moe_combine_describe_launch.argtypes = [ctypes.c_int, I64, I32, I32, ctypes.c_char_p, I32]
     L.moe_combine_describe_launch.restype = ctypes.c_int
@@ -91,7 +92,7 @@ def abi_version() -> int:
 
 def describe_launch(kind: int, num_tokens: int, hidden: int, top_k: int) -> str:
     """Launch shape an entry point would use (kind 0 bf16, 1 RMSNorm, 2 MXFP8,
-    3 RMSNorm + MXFP8)."""
+    3 RMSNorm + MXFP8, 4 MXFP4)."""
     buf = ctypes.create_string_buffer(256)
     _check("moe_combine_describe_launch",
            lib().moe_combine_describe_launch(kind, num_tokens, hidden, top_k, buf, 256))
@@ -234,3 +235,20 @@ def moe_combine_residual_rmsnorm_mxfp8(payload, src_info, router_weights, shared
         _ptr(residual_in), _ptr(gamma), float(eps), wb, _ptr(residual_out),
         _ptr(norm_out), _ptr(out_fp8), _ptr(out_scales), T, H, k, ep, mtpr, _stream(dev)))
     return residual_out, out_fp8, out_scales, norm_out
+
+
+def moe_combine_mxfp4(payload, src_info, router_weights=None, shared_out=None,
+                      out_fp4=None, out_scales=None):
+    """MXFP4 combine; returns (out_fp4 uint8 [T, H/2], two e2m1 codes per
+    byte with element 2i in the low nibble, out_scales uint8 [T, H/32] UE8M0)."""
+    dev, (T, H, k, ep, mtpr) = _common(payload, src_info, router_weights, shared_out)
+    if H % 32:
+        raise ValueError("hidden must be a multiple of 32 for MXFP4")
+    out_fp4 = _out(out_fp4, "out_fp4", torch.uint8, dev, T, H // 2,
+                   lambda: torch.empty((T, H // 2), dtype=torch.uint8, device=dev))
+    out_scales = _out(out_scales, "out_scales", torch.uint8, dev, T, H // 32,
+                      lambda: torch.empty((T, H // 32), dtype=torch.uint8, device=dev))
+    _check("moe_combine_mxfp4", lib().moe_combine_mxfp4(
+        _ptr(payload), _ptr(src_info), _ptr(router_weights), _ptr(shared_out),
+        _ptr(out_fp4), _ptr(out_scales), T, H, k, ep, mtpr, _stream(dev)))
+    return out_fp4, out_scales

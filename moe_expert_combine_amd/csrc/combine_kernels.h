@@ -28,7 +28,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-enum Epilogue { EPI_BF16 = 0, EPI_RMSNORM = 1, EPI_MXFP8 = 2, EPI_RMSNORM_MXFP8 = 3 };
+enum Epilogue { EPI_BF16 = 0, EPI_RMSNORM = 1, EPI_MXFP8 = 2, EPI_RMSNORM_MXFP8 = 3, EPI_MXFP4 = 4 };
 
 struct KernelArgs {
     const uint16_t *payload;   // [ep, mtpr, H] bf16
@@ -95,6 +95,23 @@ __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
 __device__ __forceinline__ void st_stream(uint8_t *p, u32x2 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
 }
+__device__ __forceinline__ void st_stream(uint8_t *p, unsigned v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<unsigned *>(p));
+}
+
+// fp32 magnitude bits -> float4 e2m1 code magnitude (0..7 for 0, 0.5, 1, 1.5,
+// 2, 3, 4, 6): round to nearest even on that grid, saturate at 6; e2m1 has no
+// NaN, so NaN and infinity saturate too. Integer route: at or above 1 the fp32
+// pattern is rounded to 1 mantissa bit and rebiased (127 -> 1); below 1 the
+// value is doubled (exact) and rounded to an integer number of 0.5 steps.
+__device__ __forceinline__ unsigned e2m1_mag(unsigned a) {
+    if (a > 0x7F800000u || a >= 0x40C00000u) return 7u;   // NaN, >= 6 (and inf)
+    if (a >= 0x3F800000u) {                               // >= 1
+        const unsigned r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+        return (r >> 22) - 252u;
+    }
+    return (unsigned)__builtin_rintf(__uint_as_float(a) * 2.0f);
+}
 
 // Max over the 4 lanes of a DPP quad (lanes 4m..4m+3).
 __device__ __forceinline__ int quad_max(int v) {
@@ -150,6 +167,39 @@ __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const 
             o[e >> 2] |= code << ((e & 3) * 8);
         }
         st_stream(codes + row_off + (int64_t)vi[v] * 8, o);
+        if ((threadIdx.x & 3) == 0) scales[scale_row_off + (vi[v] >> 2)] = (uint8_t)sbyte;
+    }
+}
+
+// MXFP4 quantisation (flashinfer.comm.moe_a2a_combine, Parameters
+// output_scales UE8M0 with 32 elements per scale; the MXFP4 path ignores
+// output_scalar_scale): like mx_quantize_store with the e2m1 element format,
+// whose largest value is 6 = 1.5 * 2^2, so the scale byte is the exponent
+// field of amax minus 2. Eight 4-bit codes per vector, element 2i in the low
+// nibble of byte i, stored as one 4-byte word.
+template <int V>
+__device__ __forceinline__ void mx4_quantize_store(const float (&x)[V][8], const bool (&ok)[V],
+                                                   const int (&vi)[V], int64_t code_row_off,
+                                                   int64_t scale_row_off, uint8_t *codes,
+                                                   uint8_t *scales) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        int m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = max(m, (int)(__float_as_uint(x[v][e]) & 0x7FFFFFFFu));
+        m = quad_max(m);
+        const unsigned ef = (unsigned)m >> 23;
+        const unsigned sbyte = ef == 255u ? 255u : (ef > 2u ? ef - 2u : 0u);
+        const float inv = ef == 255u ? 1.0f : __uint_as_float((254u - sbyte) << 23);
+        if (!ok[v]) continue;
+        unsigned o = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const unsigned sgn = (__float_as_uint(x[v][e]) >> 28) & 0x8u;
+            const float q = x[v][e] * inv;
+            o |= (sgn | e2m1_mag(__float_as_uint(q) & 0x7FFFFFFFu)) << (4 * e);
+        }
+        st_stream(codes + code_row_off + (int64_t)vi[v] * 4, o);
         if ((threadIdx.x & 3) == 0) scales[scale_row_off + (vi[v] >> 2)] = (uint8_t)sbyte;
     }
 }
@@ -332,9 +382,12 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
         if constexpr (EPI == EPI_RMSNORM_MXFP8)
             mx_quantize_store<V>(acc, ok, vi, row_off, (int64_t)t * (a.H >> 5),
                                  static_cast<uint8_t *>(a.out1), static_cast<uint8_t *>(a.out2));
-    } else {
+    } else if constexpr (EPI == EPI_MXFP8) {
         mx_quantize_store<V>(acc, ok, vi, row_off, (int64_t)t * (a.H >> 5),
                              static_cast<uint8_t *>(a.out0), static_cast<uint8_t *>(a.out1));
+    } else {
+        mx4_quantize_store<V>(acc, ok, vi, (int64_t)t * (a.H >> 1), (int64_t)t * (a.H >> 5),
+                              static_cast<uint8_t *>(a.out0), static_cast<uint8_t *>(a.out1));
     }
 }
 

@@ -268,6 +268,28 @@ moe_status_t moe_combine_mxfp8(const void *payload, const int32_t *src_info, con
     return launch<moe::EPI_MXFP8>(p, a, stream);
 }
 
+moe_status_t moe_combine_mxfp4(const void *payload, const int32_t *src_info, const float *router_weights,
+                               const void *shared_out, void *out_fp4, uint8_t *out_scales, int64_t num_tokens,
+                               int32_t hidden, int32_t top_k, int32_t ep_size, int64_t max_tokens_per_rank,
+                               void *stream) {
+    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
+                                   ep_size, max_tokens_per_rank);
+    if (st != MOE_OK) return st;
+    if (hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP4 (got %d)", hidden);
+    if (num_tokens == 0) return ok();
+    if (!out_fp4 || !out_scales) return fail(MOE_ERR_INVALID_ARG, "out_fp4 and out_scales are required");
+    if (!aligned(out_fp4, 4)) return fail(MOE_ERR_INVALID_ARG, "out_fp4 must be 4-byte aligned");
+    if (out_fp4 == payload || out_fp4 == shared_out || (const void *)out_scales == payload ||
+        (const void *)out_scales == shared_out || (const void *)out_scales == out_fp4)
+        return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input or each other");
+    Plan p;
+    if ((st = make_plan(moe::EPI_MXFP4, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    a.out0 = out_fp4;
+    a.out1 = out_scales;
+    return launch<moe::EPI_MXFP4>(p, a, stream);
+}
+
 moe_status_t moe_combine_residual_rmsnorm_mxfp8(const void *payload, const int32_t *src_info,
                                                 const float *router_weights, const void *shared_out,
                                                 const void *residual_in, const void *gamma, float eps,
@@ -311,13 +333,13 @@ moe_status_t moe_combine_residual_rmsnorm_mxfp8(const void *payload, const int32
 
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,
                                          int32_t buflen) {
-    if (kind < 0 || kind > 3) return fail(MOE_ERR_INVALID_ARG, "kind must be 0, 1, 2 or 3");
+    if (kind < 0 || kind > 4) return fail(MOE_ERR_INVALID_ARG, "kind must be in [0, 4]");
     if (!buf || buflen < 1) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or empty");
     moe_status_t st = check_common(reinterpret_cast<const void *>(16), reinterpret_cast<const int32_t *>(16), nullptr,
                                    nullptr, num_tokens, hidden, top_k, 1, 1);
     if (st != MOE_OK) return st;
-    if ((kind == 2 || kind == 3) && hidden % 32)
-        return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8");
+    if (kind >= 2 && hidden % 32)
+        return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8 / MXFP4");
     Plan p;
     if ((st = make_plan(kind, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
     snprintf(buf, (size_t)buflen, "threads=%d vec_per_thread=%d chunks=%d blocks=%lld slot_tile=%d masked=%d",

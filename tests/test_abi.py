@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
-              "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_describe_launch", "moe_combine_abi_version",
+              "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
+              "moe_combine_describe_launch", "moe_combine_abi_version",
               "moe_combine_status_string", "moe_combine_last_error"):
         assert n in names
 
@@ -108,6 +109,19 @@ def test_mxfp8_argument_errors():
     assert f(s=None) == INVALID
     assert f(o=5 * A + 4) == INVALID
     assert f(s=5 * A) == INVALID                 # scales alias codes
+
+
+def test_mxfp4_argument_errors():
+    L = mc.lib()
+    f = lambda H=64, o=5 * A, s=6 * A: L.moe_combine_mxfp4(A, A, A, None, o, s, 4, H, 2, 1, 8, None)
+    assert f(H=48) == INVALID
+    assert f(o=None) == INVALID
+    assert f(s=None) == INVALID
+    assert f(o=5 * A + 2) == INVALID              # 4-byte alignment
+    assert f(s=5 * A) == INVALID
+    assert "multiple of 32" in (L.moe_combine_last_error().decode() if f(H=40) else "multiple of 32")
+    assert L.moe_combine_mxfp4(None, None, None, None, None, None, 0, 64, 2, 1, 8, None) == OK
+    assert "masked=0" in mc.describe_launch(4, 16384, 7168, 8)
 
 
 def test_rmsnorm_mxfp8_argument_errors():

@@ -156,6 +156,33 @@ def check_rmsnorm_mxfp8(inp, wb, extra_rows=0, want_norm=True, what=""):
     check_mxfp8(c, sc, rc, rs, f"{what} mxfp8 of norm wb={wb}")
 
 
+def run_mxfp4(inp, extra_rows=0):
+    d = to_dev(inp)
+    T, H = inp.T, inp.H
+    codes = torch.full((T + extra_rows, H // 2), POISON8, dtype=torch.uint8, device=DEV)
+    scales = torch.full((T + extra_rows, H // 32), POISON8, dtype=torch.uint8, device=DEV)
+    mc.moe_combine_mxfp4(d["payload"], d["src_info"], d["weights"], d["shared"],
+                         out_fp4=codes, out_scales=scales)
+    torch.cuda.synchronize()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    if extra_rows:
+        assert (c[T:] == POISON8).all() and (s[T:] == POISON8).all()
+    return c[:T], s[:T]
+
+
+def check_mxfp4(codes, scales, rc, rs, what):
+    """Scales bit-exact; e2m1 codes (unpacked) within one step on <= 0.1%."""
+    np.testing.assert_array_equal(scales, rs, err_msg=f"{what}: scales")
+
+    def unpack(b):
+        b = b.astype(np.int32)
+        c = np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[0], -1)
+        return np.where(c & 0x8, -(c & 0x7), c & 0x7)
+    d = np.abs(unpack(codes) - unpack(rc))
+    assert d.max(initial=0) <= 1, f"{what}: e2m1 code distance {d.max()}"
+    assert (d != 0).mean() <= 1e-3, f"{what}: too many off-by-one e2m1 codes"
+
+
 def oracle_all(inp, kind, wb=0.0):
     if kind == "bf16":
         return oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared)
@@ -178,6 +205,9 @@ def check_all_kinds(inp, wbs=(0.0, 1.0), extra_rows=3, what=""):
         c, s = run_mxfp8(inp, extra_rows)
         rc, rs = oracle_all(inp, "mxfp8")
         check_mxfp8(c, s, rc, rs, f"{what} mxfp8")
+        c4, s4 = run_mxfp4(inp, extra_rows)
+        rc4, rs4 = oracle.combine_mxfp4(inp.payload, inp.src_info, inp.weights, inp.shared)
+        check_mxfp4(c4, s4, rc4, rs4, f"{what} mxfp4")
         if inp.residual is not None:
             for i, wb in enumerate(wbs):
                 check_rmsnorm_mxfp8(inp, wb, extra_rows, want_norm=(i == 0), what=what)
@@ -235,6 +265,16 @@ def test_golden_fixtures_on_gpu():
     for t in range(2):
         assert list(scales[t]) == fx["scales"][t]
         assert list(codes[t]) == fx["codes"][t]
+
+
+def test_golden_mxfp4_on_gpu():
+    fx = load_fixture("mxfp4_small.txt")
+    x0 = np.array(fx["x"][0], dtype=np.float32)
+    src = torch.zeros((1, 1, 2), dtype=torch.int32, device=DEV)
+    w = torch.ones((1, 1), dtype=torch.float32, device=DEV)
+    codes, scales = mc.moe_combine_mxfp4(dev16(to_bf16_bits(x0)[None, None]), src, w)
+    assert list(scales.cpu().numpy()[0]) == fx["scales"][0]
+    assert list(codes.cpu().numpy()[0]) == fx["codes"][0]
 
 
 def test_golden_rmsnorm_mxfp8_on_gpu():
@@ -350,6 +390,23 @@ def test_e4m3_conversion_every_bf16_pattern():
     np.testing.assert_array_equal(codes, rc)
 
 
+def test_e2m1_conversion_every_bf16_pattern():
+    """All 65536 bf16 patterns as single-slot sums through the MXFP4 path."""
+    H = 1024
+    allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(64, H)
+    rng = np.random.default_rng(1)
+    payload = np.concatenate([allp, rng.permutation(allp.reshape(-1)).reshape(64, H)])[None]
+    T = payload.shape[1]
+    src = np.ascontiguousarray(np.stack([np.zeros(T, np.int32), np.arange(T, dtype=np.int32)],
+                                        axis=-1)[:, None, :])
+    w = np.ones((T, 1), np.float32)
+    codes, scales = mc.moe_combine_mxfp4(dev16(payload), torch.from_numpy(src).to(DEV),
+                                         torch.from_numpy(w).to(DEV))
+    rc, rs = oracle.combine_mxfp4(payload, src, w)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
 @pytest.mark.parametrize("tile", ["64x1", "64x2", "64x4", "128x2", "128x4", "256x1", "256x4",
                                   "512x8", "512x4", "1024x1", "448x2", "896x1", "192x8", "1024x2"])
 def test_every_tile_shape(monkeypatch, tile):
@@ -361,6 +418,8 @@ def test_every_tile_shape(monkeypatch, tile):
     check_bf16(run_combine(inp, 2), oracle_all(inp, "bf16"), 1e-3, tile)
     c_, s_ = run_mxfp8(inp, 2)
     check_mxfp8(c_, s_, *oracle_all(inp, "mxfp8"), tile)
+    c4, s4 = run_mxfp4(inp, 2)
+    check_mxfp4(c4, s4, *oracle.combine_mxfp4(inp.payload, inp.src_info, inp.weights, inp.shared), tile)
     if nt * v * 8 >= inp.H:
         ro, no = run_rmsnorm(inp, 0.0, 2)
         rro, rno = oracle_all(inp, "rmsnorm", 0.0)
@@ -370,6 +429,15 @@ def test_every_tile_shape(monkeypatch, tile):
 
 
 # ----------------------------------------------- full workload sizes
+
+@pytest.mark.slow
+def test_full_size_mxfp4():
+    """MXFP4 output on the MXFP8 workload's inputs (T=16384, H=7168)."""
+    inp = gen.make_inputs("mxfp8", 0)
+    c, s = run_mxfp4(inp)
+    check_mxfp4(c, s, *oracle.combine_mxfp4(inp.payload, inp.src_info, inp.weights, inp.shared),
+                "mxfp4 workload")
+
 
 @pytest.mark.slow
 @pytest.mark.parametrize("wb", [0.0, 1.0])
