@@ -17,6 +17,9 @@ the documentation pages it follows, is stated in ``oracle.c``:
                                    quantised to MXFP8;
 * ``combine_mxfp4``             -- + MXFP4 e2m1 codes (two per byte) and
                                    UE8M0 scales / 32;
+* ``reduce_dense``              -- weighted sum of expert-major dense inputs
+                                   [n_in, T, H] (+ token input, + residual
+                                   and RMSNorm): the local reduce;
 * ``routed_sum_f32``            -- the fp32 sum before any epilogue;
 * ``bf16_rne``, ``e4m3_rne_sat``, ``mx_exponent``, ``e2m1_rne_sat``,
   ``mx4_exponent`` -- the scalar conversions.
@@ -72,6 +75,8 @@ def _L():
         lib.oracle_combine_residual_rmsnorm_mxfp8.argtypes = (
             common + [P, P, F, F, P, P, P, P] + dims)
         lib.oracle_combine_mxfp4.argtypes = common + [P, P] + dims
+        lib.oracle_reduce_dense.argtypes = [P, I, P, P, P, P, F, F, P, P, I64, I64]
+        lib.oracle_reduce_dense.restype = I
         for f in ("oracle_routed_sum_f32", "oracle_combine",
                   "oracle_combine_residual_rmsnorm", "oracle_combine_mxfp8",
                   "oracle_combine_residual_rmsnorm_mxfp8", "oracle_combine_mxfp4"):
@@ -213,6 +218,32 @@ def combine_mxfp4(payload, src_info, weights=None, shared=None, checked=True):
                                   _ptr(shared), _ptr(codes), _ptr(scales), T, H,
                                   k, ep, mtpr, int(checked)))
     return codes, scales
+
+
+def reduce_dense(x, scales=None, tok=None, residual=None, gamma=None, eps=1e-6,
+                 weight_bias=0.0):
+    """x: bf16 bits [n_in, T, H]; scales fp32 [T, n_in] or None; tok bf16
+    [T, H] or None. Returns out bf16 [T, H], or (residual_out, norm_out)
+    when residual and gamma are given."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    n_in, T, H = x.shape
+    if scales is not None:
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        assert scales.shape == (T, n_in)
+    if tok is not None:
+        tok = np.ascontiguousarray(tok, dtype=np.uint16)
+        assert tok.shape == (T, H)
+    out = np.empty((T, H), dtype=np.uint16)
+    no = None
+    if residual is not None:
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
+        gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+        no = np.empty((T, H), dtype=np.uint16)
+    _rc(_L().oracle_reduce_dense(_ptr(x), n_in, _ptr(scales), _ptr(tok), _ptr(residual),
+                                 _ptr(gamma), float(eps),
+                                 float(0.0 if weight_bias is None else weight_bias),
+                                 _ptr(out), _ptr(no), T, H))
+    return out if residual is None else (out, no)
 
 
 def e2m1_rne_sat(x: float) -> int:

@@ -399,6 +399,55 @@ int oracle_combine_mxfp4(const uint16_t *payload, const int32_t *src_info,
     return 0;
 }
 
+/* Dense MoE reduction: inputs are expert-major rows [n_in, T, H] (one row per
+ * (input, token); for the local reduce that replaces the all-to-all, the
+ * inputs are the n_in partial sums of the ranks), per-(token, input) fp32
+ * scales or none, and an optional token input added unweighted:
+ *   out[t, h] = bf16_rne( (sum over i ascending of s[t, i] * x[i, t, h]) + tok[t, h] )
+ * with one fp32 fused multiply-add per input from +0, then one fp32 add.
+ * Sources: flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters
+ * moe_reduction_scale_input, moe_reduction_active_experts_token_input and
+ * moe_reduction_token_input; Struct_ep_combine_skip_a2a, Parameters
+ * skip_a2a and allreduce_world_size (reduce locally instead of exchanging).
+ * The residual + RMSNorm epilogue, if residual_in is given, is the one of
+ * oracle_combine_residual_rmsnorm (out is then residual_out). */
+int oracle_reduce_dense(const uint16_t *x, int n_in, const float *scales,
+                        const uint16_t *tok, const uint16_t *residual_in,
+                        const uint16_t *gamma, float eps, float weight_bias,
+                        uint16_t *out, uint16_t *norm_out, int64_t T, int64_t H)
+{
+    if (T < 0 || H <= 0 || n_in < 1) return 2;
+    if (residual_in && (!gamma || !norm_out)) return 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int i = 0; i < n_in; ++i) {
+                float s = scales ? scales[t * n_in + i] : 1.0f;
+                acc = fmaf(s, bf16_to_float(x[((int64_t)i * T + t) * H + h]), acc);
+            }
+            if (tok)
+                acc = acc + bf16_to_float(tok[t * H + h]);
+            if (residual_in)
+                acc = acc + bf16_to_float(residual_in[t * H + h]);
+            uint16_t o = oracle_bf16_rne(acc);
+            out[t * H + h] = o;
+            double v = (double)bf16_to_float(o);
+            ss += v * v;
+        }
+        if (!residual_in)
+            continue;
+        double rstd = 1.0 / sqrt(ss / (double)H + (double)eps);
+        for (int64_t h = 0; h < H; ++h) {
+            double v = (double)bf16_to_float(out[t * H + h]);
+            float g = bf16_to_float(gamma[h]) + weight_bias;
+            norm_out[t * H + h] = oracle_bf16_rne((float)(v * rstd * (double)g));
+        }
+    }
+    return 0;
+}
+
 /* ---- threading ----------------------------------------------------------- */
 
 void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

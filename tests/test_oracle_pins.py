@@ -650,3 +650,45 @@ def test_mxfp4_blocks_brute_force():
                 c = (byte >> 4) if i % 2 else (byte & 0xF)
                 q = blk[i] * 2.0 ** -e
                 assert c == nearest_e2m1(q), (t, b, i, q)
+
+
+# ------------------------------------------------- dense / local reduce
+
+def _dense_case(seed, n_in=6, T=20, H=256):
+    rng = np.random.default_rng(seed)
+    x = to_bf16_bits(rng.standard_normal((n_in, T, H)))
+    sc = rng.random((T, n_in)).astype(np.float32)
+    tok = to_bf16_bits(rng.standard_normal((T, H)) * 0.5)
+    res = to_bf16_bits(rng.standard_normal((T, H)))
+    gam = to_bf16_bits(1 + 0.1 * rng.standard_normal(H))
+    ident = np.stack([np.broadcast_to(np.arange(n_in, dtype=np.int32), (T, n_in)),
+                      np.broadcast_to(np.arange(T, dtype=np.int32)[:, None], (T, n_in))], axis=-1)
+    return x, sc, tok, res, gam, np.ascontiguousarray(ident)
+
+
+def test_reduce_dense_equals_combine_with_identity_map():
+    """Input i of token t read through the slot map (i, t): the combine's
+    pinned definition gives the same bits, with and without scales, token
+    input, residual + RMSNorm."""
+    x, sc, tok, res, gam, ident = _dense_case(0)
+    for s_, t_ in [(sc, tok), (None, None), (sc, None), (None, tok)]:
+        np.testing.assert_array_equal(oracle.reduce_dense(x, s_, t_),
+                                      oracle.combine(x, ident, s_, t_))
+    ro, no = oracle.reduce_dense(x, sc, tok, res, gam, 1e-6, 1.0)
+    ro2, no2 = oracle.combine_residual_rmsnorm(x, ident, sc, tok, res, gam, 1e-6, 1.0)
+    np.testing.assert_array_equal(ro, ro2)
+    np.testing.assert_array_equal(no, no2)
+
+
+def test_reduce_dense_special_cases():
+    x, sc, tok, res, gam, ident = _dense_case(1, n_in=1)
+    np.testing.assert_array_equal(oracle.reduce_dense(x), x[0])           # one input
+    x4 = np.zeros((4,) + x.shape[1:], np.uint16)
+    x4[2] = x[0]
+    np.testing.assert_array_equal(oracle.reduce_dense(x4), x[0])          # others zero
+    # exact dyadic sums
+    rng = np.random.default_rng(2)
+    v = rng.integers(-8, 9, size=(5, 7, 64)) / 8.0
+    s = (rng.integers(1, 5, size=(7, 5)) / 4.0).astype(np.float32)
+    exact = np.einsum("ti,ith->th", s.astype(np.float64), v)
+    np.testing.assert_array_equal(oracle.reduce_dense(to_bf16_bits(v), s), to_bf16_bits(exact))
