@@ -29,7 +29,8 @@ METRIC = "combined tokens/s + achieved HBM GB/s (% peak), T=4096 H=7168 top_k=8"
 PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 
 KIND = {"dsv3": "bf16", "skewed": "bf16", "tiny": "bf16", "rmsnorm": "rmsnorm",
-        "mxfp8": "mxfp8", "rmsnorm_mxfp8": "rmsnorm_mxfp8", "mxfp4": "mxfp4"}
+        "mxfp8": "mxfp8", "rmsnorm_mxfp8": "rmsnorm_mxfp8", "mxfp4": "mxfp4",
+        "dense8": "dense"}
 # workloads that reuse another workload's inputs
 INPUTS = {"rmsnorm_mxfp8": "rmsnorm", "mxfp4": "mxfp8"}
 DESCR = {
@@ -39,6 +40,7 @@ DESCR = {
     "mxfp8": "moe combine T=16384 H=7168 top_k=8 E=256 ep=8, MXFP8 e4m3 out + UE8M0/32 scales",
     "tiny": "moe combine T=64 H=1024 top_k=2 E=8 ep=1, bf16 out",
     "mxfp4": "moe combine T=16384 H=7168 top_k=8 E=256 ep=8, MXFP4 e2m1 out + UE8M0/32 scales",
+    "dense8": "local reduce of 8 partial sums [4096, 7168] bf16 (skip_a2a), bf16 out",
     "rmsnorm_mxfp8": "moe combine + residual + RMSNorm T=2048 H=7168 top_k=8 E=256 ep=8, weight_bias=1, normalised row as MXFP8 e4m3 + UE8M0/32",
 }
 
@@ -95,16 +97,24 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {args.workload} seed={args.seed}", file=sys.stderr, flush=True)
-    inp = gen.make_inputs(INPUTS.get(args.workload, args.workload), args.seed)
-    T, H, k, ep, mtpr = inp.T, inp.H, inp.k, inp.ep, inp.mtpr
-    algo_bytes = gen.algorithmic_bytes(inp, kind)
 
     def d16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    base = dict(payload=d16(inp.payload), src=torch.from_numpy(inp.src_info).to(dev),
-                w=torch.from_numpy(inp.weights).to(dev),
-                shared=None if inp.shared is None else d16(inp.shared))
+    if kind == "dense":
+        inp = gen.make_dense_inputs(args.workload, args.seed)
+        T, H, k, ep, mtpr = inp.T, inp.H, inp.n_in, inp.n_in, inp.T
+        algo_bytes = gen.dense_algorithmic_bytes(inp)
+        base = dict(payload=d16(inp.x), src=None, w=None, shared=None)
+        kept = T * k
+    else:
+        inp = gen.make_inputs(INPUTS.get(args.workload, args.workload), args.seed)
+        T, H, k, ep, mtpr = inp.T, inp.H, inp.k, inp.ep, inp.mtpr
+        algo_bytes = gen.algorithmic_bytes(inp, kind)
+        base = dict(payload=d16(inp.payload), src=torch.from_numpy(inp.src_info).to(dev),
+                    w=torch.from_numpy(inp.weights).to(dev),
+                    shared=None if inp.shared is None else d16(inp.shared))
+        kept = inp.meta["kept_slots"]
     if kind in ("rmsnorm", "rmsnorm_mxfp8"):
         base["res"] = d16(inp.residual)
         base["gamma"] = d16(inp.gamma)
@@ -113,7 +123,7 @@ def main():
     sets = []
     for i in range(nsets):
         s = {kk: (None if v is None else (v if i == 0 else v.clone())) for kk, v in base.items()}
-        if kind == "bf16":
+        if kind in ("bf16", "dense"):
             s["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         elif kind == "rmsnorm":
             s["ro"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -137,7 +147,10 @@ def main():
     P = lambda t: None if t is None else t.data_ptr()
     calls = []
     for s in sets:
-        if kind == "bf16":
+        if kind == "dense":
+            a = (P(s["payload"]), k, None, None, P(s["out"]), T, H, sptr)
+            calls.append((L.moe_reduce_dense, a))
+        elif kind == "bf16":
             a = (P(s["payload"]), P(s["src"]), P(s["w"]), P(s["shared"]), P(s["out"]),
                  T, H, k, ep, mtpr, sptr)
             calls.append((L.moe_combine, a))
@@ -223,7 +236,9 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        if kind == "bf16":
+        if kind == "dense":
+            run = lambda: oracle.reduce_dense(inp.x)
+        elif kind == "bf16":
             run = lambda: oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared, checked=False)
         elif kind == "rmsnorm":
             run = lambda: oracle.combine_residual_rmsnorm(inp.payload, inp.src_info, inp.weights,
@@ -257,9 +272,9 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": DESCR[args.workload], "num_tokens": T, "hidden": H,
                    "top_k": k, "ep_size": ep, "max_tokens_per_rank": mtpr,
-                   "kept_slots": inp.meta["kept_slots"], "io_dtype": "bf16",
+                   "kept_slots": kept, "io_dtype": "bf16",
                    "seed": args.seed, "input_sets": nsets,
-                   "launch": mc.describe_launch({"bf16": 0, "rmsnorm": 1, "mxfp8": 2,
+                   "launch": mc.describe_launch({"bf16": 0, "dense": 0, "rmsnorm": 1, "mxfp8": 2,
                                                  "rmsnorm_mxfp8": 3, "mxfp4": 4}[kind], T, H, k)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,

@@ -38,12 +38,13 @@ import numpy as np
 import torch
 
 __all__ = ["CONFIGS", "Inputs", "make_inputs", "dispatch_slots",
-           "scatter_rows", "normal_bf16", "algorithmic_bytes"]
+           "scatter_rows", "normal_bf16", "algorithmic_bytes", "DenseInputs",
+           "make_dense_inputs", "DENSE_CONFIGS"]
 
 _BLOCK = 1 << 22  # elements per independently seeded block of a normal tensor
 
 # Stream ids of the large normal tensors (the spawn_key's first element).
-_S_PAYLOAD, _S_SHARED, _S_RESIDUAL, _S_GAMMA = 1, 2, 3, 4
+_S_PAYLOAD, _S_SHARED, _S_RESIDUAL, _S_GAMMA, _S_DENSE = 1, 2, 3, 4, 5
 
 # The five synthetic workloads (sizes of the combine; see the DESIGN notes on
 # the input recipe for every choice the workload text leaves open).
@@ -336,3 +337,67 @@ def algorithmic_bytes(inp: Inputs, kind: str = "bf16") -> int:
         raise ValueError(kind)
     return int(b)
 
+
+
+# Dense (expert-major) inputs of the local reduce: n_in buffers [T, H].
+DENSE_CONFIGS = {
+    # 8 partial sums of [4096, 7168] (one per simulated rank), unit scales
+    "dense8": dict(n_in=8, T=4096, H=7168, scales=False),
+}
+
+
+@dataclasses.dataclass
+class DenseInputs:
+    x: np.ndarray                  # uint16 [n_in, T, H]
+    scales: np.ndarray | None      # float32 [T, n_in]
+    tok: np.ndarray | None         # uint16 [T, H]
+    residual: np.ndarray | None    # uint16 [T, H]
+    gamma: np.ndarray | None       # uint16 [H]
+    eps: float
+
+    @property
+    def n_in(self):
+        return self.x.shape[0]
+
+    @property
+    def T(self):
+        return self.x.shape[1]
+
+    @property
+    def H(self):
+        return self.x.shape[2]
+
+
+def make_dense_inputs(cfg, seed: int = 0, **override) -> DenseInputs:
+    """Expert-major inputs x [n_in, T, H] bf16 N(0,1); scales [T, n_in] as a
+    softmax of N(0,1) logits (if ``scales``); optional token input N(0, sd),
+    residual N(0, sd) and gamma N(1, sd)."""
+    c = dict(DENSE_CONFIGS[cfg]) if isinstance(cfg, str) else dict(cfg)
+    c.update(override)
+    n_in, T, H = c["n_in"], c["T"], c["H"]
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    scales = _softmax_weights(rng, T, n_in) if c.get("scales", True) else None
+    x = normal_bf16((n_in, T, H), seed, _S_DENSE)
+    tok = (normal_bf16((T, H), seed, _S_SHARED, 0.0, c["token_sd"])
+           if c.get("token_sd") is not None else None)
+    res = (normal_bf16((T, H), seed, _S_RESIDUAL, 0.0, c["residual_sd"])
+           if c.get("residual_sd") is not None else None)
+    gam = (normal_bf16((H,), seed, _S_GAMMA, 1.0, c.get("gamma_sd", 0.1))
+           if c.get("residual_sd") is not None else None)
+    return DenseInputs(x=x, scales=scales, tok=tok, residual=res, gamma=gam,
+                       eps=float(c.get("eps", 1e-6)))
+
+
+def dense_algorithmic_bytes(d: DenseInputs, rmsnorm: bool = False) -> int:
+    """n_in rows per token + scales + token input (+ residual, gamma) + outputs."""
+    T, H, n = d.T, d.H, d.n_in
+    b = n * T * H * 2 + (T * n * 4 if d.scales is not None else 0)
+    if d.tok is not None:
+        b += T * H * 2
+    b += T * H * 2
+    if rmsnorm:
+        b += T * H * 2 + H * 2 + T * H * 2
+    return int(b)
+
+
+__all__.append("dense_algorithmic_bytes")

@@ -207,6 +207,46 @@ moe_status_t moe_combine_mxfp4(const void *payload, const int32_t *src_info,
                                int64_t max_tokens_per_rank, void *stream);
 
 /*
+ * Dense MoE reduction: the local reduce of the expert-parallel combine. It
+ * replaces the all-to-all exchange when skip_a2a is set, and it is the MoE
+ * reduction in front of the all-reduce of the allreduce-fusion kernel.
+ *
+ * inputs is [n_in, num_tokens, hidden] bf16, expert-major: row t of input i
+ * is expert i's (or rank i's partial) output for token t. scales is
+ * [num_tokens, n_in] fp32, or NULL for unit scales, which gives the plain
+ * sum of n_in partial buffers. token_input is [num_tokens, hidden] bf16, or
+ * NULL.
+ *   acc = +0;  acc = fmaf(scales[t, i], inputs[i, t, h], acc) for i ascending
+ *   acc += token_input[t, h];  out[t, h] = bf16(acc)
+ * This is moe_combine with the slot map (rank, row) = (i, t). Arguments
+ * follow that entry point's rules, with 1 <= n_in <= 32.
+ *
+ * Sources: Struct_ep_combine_skip_a2a, Parameters skip_a2a and
+ * allreduce_world_size; flashinfer.comm.trtllm_moe_allreduce_fusion,
+ * Parameters moe_reduction_scale_input,
+ * moe_reduction_active_experts_token_input and moe_reduction_token_input.
+ */
+moe_status_t moe_reduce_dense(const void *inputs, int32_t n_in,
+                              const float *scales, const void *token_input,
+                              void *out, int64_t num_tokens, int32_t hidden,
+                              void *stream);
+
+/*
+ * moe_reduce_dense followed by the residual add and RMSNorm of
+ * moe_combine_residual_rmsnorm: the single-GPU body of the MoE reduction
+ * + residual + RMSNorm fusion (the all-reduce between them has one
+ * participant here). Outputs and aliasing follow
+ * moe_combine_residual_rmsnorm.
+ * Source: flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters
+ * residual_in, rms_gamma, rms_eps, residual_out, norm_out, weight_bias.
+ */
+moe_status_t moe_reduce_dense_residual_rmsnorm(
+    const void *inputs, int32_t n_in, const float *scales,
+    const void *token_input, const void *residual_in, const void *gamma,
+    float eps, float weight_bias, void *residual_out, void *norm_out,
+    int64_t num_tokens, int32_t hidden, void *stream);
+
+/*
  * Describes the launch an entry point would make for these sizes, without
  * touching the GPU. kind: 0 = moe_combine, 1 = residual + RMSNorm,
  * 2 = MXFP8, 3 = residual + RMSNorm + MXFP8, 4 = MXFP4.

@@ -26,6 +26,7 @@ from . import _build
 
 __all__ = ["moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
            "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
+           "moe_reduce_dense", "moe_reduce_dense_residual_rmsnorm",
            "describe_launch", "abi_version", "lib", "library_path",
            "MoeCombineError"]
 
@@ -55,6 +56,10 @@ def _load():
     L.moe_combine_mxfp8.argtypes = [P, P, P, P, P, P] + dims
     L.moe_combine_residual_rmsnorm_mxfp8.argtypes = [P, P, P, P, P, P, F, F, P, P, P, P] + dims
     L.moe_combine_mxfp4.argtypes = [P, P, P, P, P, P] + dims
+    L.moe_reduce_dense.argtypes = [P, I32, P, P, P, I64, I32, P]
+    L.moe_reduce_dense.restype = ctypes.c_int
+    L.moe_reduce_dense_residual_rmsnorm.argtypes = [P, I32, P, P, P, P, F, F, P, P, I64, I32, P]
+    L.moe_reduce_dense_residual_rmsnorm.restype = ctypes.c_int
     for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
               "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4"):
         getattr(L, f).restype = ctypes.c_int
@@ -252,3 +257,51 @@ def moe_combine_mxfp4(payload, src_info, router_weights=None, shared_out=None,
         _ptr(payload), _ptr(src_info), _ptr(router_weights), _ptr(shared_out),
         _ptr(out_fp4), _ptr(out_scales), T, H, k, ep, mtpr, _stream(dev)))
     return out_fp4, out_scales
+
+
+def _dense(inputs, scales, token_input):
+    if not isinstance(inputs, torch.Tensor) or inputs.device.type != "cuda":
+        raise ValueError("inputs must be a GPU tensor")
+    dev = inputs.device
+    _need(inputs, "inputs", torch.bfloat16, dev, 3)
+    n_in, T, H = inputs.shape
+    if scales is not None:
+        _need(scales, "scales", torch.float32, dev, 2)
+        if tuple(scales.shape) != (T, n_in):
+            raise ValueError(f"scales must be [{T}, {n_in}]")
+    if token_input is not None:
+        _need(token_input, "token_input", torch.bfloat16, dev, 2)
+        if tuple(token_input.shape) != (T, H):
+            raise ValueError(f"token_input must be [{T}, {H}]")
+    return dev, n_in, T, H
+
+
+def moe_reduce_dense(inputs, scales=None, token_input=None, out=None):
+    """Weighted sum of expert-major inputs [n_in, T, H] (unit scales if None:
+    the plain sum of n_in partial buffers), plus token_input; bf16 [T, H]."""
+    dev, n_in, T, H = _dense(inputs, scales, token_input)
+    out = _out(out, "out", torch.bfloat16, dev, T, H,
+               lambda: torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+    _check("moe_reduce_dense", lib().moe_reduce_dense(
+        _ptr(inputs), n_in, _ptr(scales), _ptr(token_input), _ptr(out), T, H, _stream(dev)))
+    return out
+
+
+def moe_reduce_dense_residual_rmsnorm(inputs, scales, token_input, residual_in, gamma, eps,
+                                      weight_bias=0.0, residual_out=None, norm_out=None):
+    """moe_reduce_dense + residual add + RMSNorm; returns (residual_out, norm_out)."""
+    dev, n_in, T, H = _dense(inputs, scales, token_input)
+    _need(residual_in, "residual_in", torch.bfloat16, dev, 2)
+    if residual_in.shape[0] < T or residual_in.shape[1] != H:
+        raise ValueError(f"residual_in must be [>= {T}, {H}]")
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    if gamma.shape[0] != H:
+        raise ValueError(f"gamma must be [{H}]")
+    mk = lambda: torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    residual_out = _out(residual_out, "residual_out", torch.bfloat16, dev, T, H, mk)
+    norm_out = _out(norm_out, "norm_out", torch.bfloat16, dev, T, H, mk)
+    wb = 0.0 if weight_bias is None else float(weight_bias)
+    _check("moe_reduce_dense_residual_rmsnorm", lib().moe_reduce_dense_residual_rmsnorm(
+        _ptr(inputs), n_in, _ptr(scales), _ptr(token_input), _ptr(residual_in), _ptr(gamma),
+        float(eps), wb, _ptr(residual_out), _ptr(norm_out), T, H, _stream(dev)))
+    return residual_out, norm_out

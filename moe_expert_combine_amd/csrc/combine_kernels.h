@@ -32,7 +32,7 @@ enum Epilogue { EPI_BF16 = 0, EPI_RMSNORM = 1, EPI_MXFP8 = 2, EPI_RMSNORM_MXFP8 
 
 struct KernelArgs {
     const uint16_t *payload;   // [ep, mtpr, H] bf16
-    const int32_t *src_info;   // [T, k, 2]
+    const int32_t *src_info;   // [T, k, 2]; null: slot j of token t is row t of input j
     const float *weights;      // [T, k] or null (unit weights)
     const uint16_t *shared;    // [T, H] or null
     const uint16_t *residual;  // [T, H]   (RMSNorm)
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
         }
     }
 
-    const int32_t *__restrict__ si = a.src_info + (int64_t)t * a.k * 2;
+    const int32_t *__restrict__ si = a.src_info ? a.src_info + (int64_t)t * a.k * 2 : nullptr;
     const float *__restrict__ wt = a.weights ? a.weights + (int64_t)t * a.k : nullptr;
 
     for (int g = 0; g < a.k; g += KT) {
@@ -258,7 +258,16 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
         bool valid[KT];
         float w[KT];
         int r[KT], row[KT];
-        if (g + KT <= a.k) {
+        if (!a.src_info) {
+            // dense inputs [k, T, H]: slot j of token t is row t of input j
+#pragma unroll
+            for (int jj = 0; jj < KT; ++jj) {
+                const int j = g + jj;
+                r[jj] = j < a.k ? j : -1;
+                row[jj] = t;
+                w[jj] = (j < a.k && wt) ? wt[j] : 1.0f;
+            }
+        } else if (g + KT <= a.k) {
             // full group: straight-line loads that merge into wide scalar loads
 #pragma unroll
             for (int jj = 0; jj < KT; ++jj) {

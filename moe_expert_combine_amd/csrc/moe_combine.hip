@@ -331,6 +331,60 @@ moe_status_t moe_combine_residual_rmsnorm_mxfp8(const void *payload, const int32
     return launch<moe::EPI_RMSNORM_MXFP8>(p, a, stream);
 }
 
+static moe_status_t check_dense(const void *inputs, int32_t n_in, const float *scales, const void *token_input,
+                                int64_t T, int32_t H) {
+    if (n_in < 1 || n_in > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "n_in must be in [1, %d] (got %d)", kMaxTopK, n_in);
+    moe_status_t st = check_common(inputs, reinterpret_cast<const int32_t *>(16), scales, token_input, T, H, n_in,
+                                   n_in, T > 0 ? T : 1);
+    if (st != MOE_OK) return st;
+    if (T > 0 && !inputs) return fail(MOE_ERR_INVALID_ARG, "inputs is NULL");
+    return MOE_OK;
+}
+
+moe_status_t moe_reduce_dense(const void *inputs, int32_t n_in, const float *scales, const void *token_input,
+                              void *out, int64_t num_tokens, int32_t hidden, void *stream) {
+    moe_status_t st = check_dense(inputs, n_in, scales, token_input, num_tokens, hidden);
+    if (st != MOE_OK) return st;
+    if (num_tokens == 0) return ok();
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if (out == inputs || out == token_input) return fail(MOE_ERR_INVALID_ARG, "out must not alias an input");
+    Plan p;
+    if ((st = make_plan(moe::EPI_BF16, num_tokens, hidden, n_in, &p)) != MOE_OK) return st;
+    moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, num_tokens, p);
+    a.out0 = out;
+    return launch<moe::EPI_BF16>(p, a, stream);
+}
+
+moe_status_t moe_reduce_dense_residual_rmsnorm(const void *inputs, int32_t n_in, const float *scales,
+                                               const void *token_input, const void *residual_in, const void *gamma,
+                                               float eps, float weight_bias, void *residual_out, void *norm_out,
+                                               int64_t num_tokens, int32_t hidden, void *stream) {
+    moe_status_t st = check_dense(inputs, n_in, scales, token_input, num_tokens, hidden);
+    if (st != MOE_OK) return st;
+    Plan p;
+    if ((st = make_plan(moe::EPI_RMSNORM, num_tokens, hidden, n_in, &p)) != MOE_OK) return st;
+    if (num_tokens == 0) return ok();
+    if (!residual_in || !gamma || !residual_out || !norm_out)
+        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out are required");
+    if (!aligned(residual_in, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) || !aligned(norm_out, 16))
+        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out must be 16-byte aligned");
+    if (norm_out == residual_out || norm_out == residual_in)
+        return fail(MOE_ERR_INVALID_ARG, "norm_out must differ from residual_in and residual_out");
+    const void *outs[2] = {residual_out, norm_out};
+    for (const void *o : outs)
+        if (o == inputs || o == token_input || o == gamma) return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input");
+    if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+    moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, num_tokens, p);
+    a.residual = static_cast<const uint16_t *>(residual_in);
+    a.gamma = static_cast<const uint16_t *>(gamma);
+    a.out0 = residual_out;
+    a.out1 = norm_out;
+    a.eps = eps;
+    a.wb = weight_bias;
+    return launch<moe::EPI_RMSNORM>(p, a, stream);
+}
+
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,
                                          int32_t buflen) {
     if (kind < 0 || kind > 4) return fail(MOE_ERR_INVALID_ARG, "kind must be in [0, 4]");

@@ -20,13 +20,14 @@ OK, INVALID, UNSUPPORTED = 0, 1, 2
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_combine\w*)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
               "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
+              "moe_reduce_dense", "moe_reduce_dense_residual_rmsnorm",
               "moe_combine_describe_launch", "moe_combine_abi_version",
               "moe_combine_status_string", "moe_combine_last_error"):
         assert n in names
@@ -122,6 +123,25 @@ def test_mxfp4_argument_errors():
     assert "multiple of 32" in (L.moe_combine_last_error().decode() if f(H=40) else "multiple of 32")
     assert L.moe_combine_mxfp4(None, None, None, None, None, None, 0, 64, 2, 1, 8, None) == OK
     assert "masked=0" in mc.describe_launch(4, 16384, 7168, 8)
+
+
+def test_reduce_dense_argument_errors():
+    L = mc.lib()
+    f = lambda x=A, n=4, s=A, tok=None, o=2 * A, T=4, H=64: L.moe_reduce_dense(x, n, s, tok, o, T, H, None)
+    assert f(n=0) == INVALID and "n_in" in L.moe_combine_last_error().decode()
+    assert f(n=33) == INVALID
+    assert f(x=None) == INVALID
+    assert f(o=None) == INVALID
+    assert f(o=A) == INVALID                       # out aliases inputs
+    assert f(H=12) == INVALID
+    assert f(x=A + 8) == INVALID
+    assert f(tok=A + 8) == INVALID
+    assert f(T=0, x=None, o=None) == OK
+    g = lambda ro=5 * A, no=6 * A, res=3 * A: L.moe_reduce_dense_residual_rmsnorm(
+        A, 4, None, None, res, 4 * A, 1e-6, 0.0, ro, no, 4, 64, None)
+    assert g(no=5 * A) == INVALID
+    assert g(res=None) == INVALID
+    assert g(no=3 * A) == INVALID
 
 
 def test_rmsnorm_mxfp8_argument_errors():

@@ -464,3 +464,59 @@ def test_full_size_workloads(name):
         check_mxfp8(c, s, *oracle_all(inp, "mxfp8"), name)
     else:
         check_bf16(run_combine(inp), oracle_all(inp, "bf16"), 1e-3, name)
+
+
+# ------------------------------------------------- dense / local reduce
+
+@pytest.mark.parametrize("n_in,T,H,scales,tok", [
+    (1, 5, 8, False, False), (2, 33, 264, True, True), (8, 64, 7168, False, False),
+    (13, 9, 1032, True, False), (32, 3, 512, True, True), (4, 17, 4096, False, True)])
+def test_reduce_dense(n_in, T, H, scales, tok):
+    d = gen.make_dense_inputs(dict(n_in=n_in, T=T, H=H, scales=scales,
+                                   token_sd=0.5 if tok else None, residual_sd=1.0), seed=n_in)
+    x = dev16(d.x)
+    sc = None if d.scales is None else torch.from_numpy(d.scales).to(DEV)
+    tk = None if d.tok is None else dev16(d.tok)
+    out = poisoned16(T, H, 2)
+    mc.moe_reduce_dense(x, sc, tk, out=out)
+    torch.cuda.synchronize()
+    o = host16(out)
+    assert (o[T:] == POISON16).all()
+    check_bf16(o[:T], oracle.reduce_dense(d.x, d.scales, d.tok), 1e-3, "reduce_dense")
+    if H % 8 == 0 and H <= 32768:
+        ro, no = mc.moe_reduce_dense_residual_rmsnorm(x, sc, tk, dev16(d.residual), dev16(d.gamma),
+                                                      d.eps, 1.0)
+        rro, rno = oracle.reduce_dense(d.x, d.scales, d.tok, d.residual, d.gamma, d.eps, 1.0)
+        check_bf16(host16(ro), rro, 1e-3, "reduce_dense residual_out")
+        check_bf16(host16(no), rno, 1e-3, "reduce_dense norm_out")
+
+
+def test_skip_a2a_partials_then_local_reduce():
+    """Each simulated rank combines only the slots it hosts (other slots
+    dropped), writing a bf16 partial; the local reduce sums the partials.
+    The same pipeline in the oracle gives the same bits."""
+    inp = gen.make_inputs(dict(T=256, H=2048, E=64, ep=8, k=8), seed=5)
+    d = to_dev(inp)
+    parts, ref_parts = [], []
+    for r in range(inp.ep):
+        src = inp.src_info.copy()
+        src[src[..., 0] != r] = -1
+        parts.append(mc.moe_combine(d["payload"], torch.from_numpy(src).to(DEV), d["weights"]))
+        ref_parts.append(oracle.combine(inp.payload, src, inp.weights))
+    out = mc.moe_reduce_dense(torch.stack(parts).contiguous())
+    ref = oracle.reduce_dense(np.stack(ref_parts))
+    np.testing.assert_array_equal(host16(out), ref)
+    # and it differs from the direct combine only by the roundings of the
+    # partials (<= half a bf16 step of each) and of the two results
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    direct = f(oracle.combine(inp.payload, inp.src_info, inp.weights))
+    bound = sum(np.abs(f(p_)) for p_ in ref_parts) * 2.0 ** -8 \
+        + (np.abs(direct) + np.abs(f(ref))) * 2.0 ** -8 + 1e-30
+    assert (np.abs(f(ref) - direct) <= bound).all()
+
+
+@pytest.mark.slow
+def test_full_size_dense8():
+    d = gen.make_dense_inputs("dense8", 0)
+    out = mc.moe_reduce_dense(dev16(d.x))
+    check_bf16(host16(out), oracle.reduce_dense(d.x), 1e-3, "dense8")
