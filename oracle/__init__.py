@@ -20,6 +20,8 @@ the documentation pages it follows, is stated in ``oracle.c``:
 * ``reduce_dense``              -- weighted sum of expert-major dense inputs
                                    [n_in, T, H] (+ token input, + residual
                                    and RMSNorm): the local reduce;
+* ``dispatch``                  -- the forward scatter the combine inverts
+                                   (stable by expert, capacity, receive counts);
 * ``routed_sum_f32``            -- the fp32 sum before any epilogue;
 * ``bf16_rne``, ``e4m3_rne_sat``, ``mx_exponent``, ``e2m1_rne_sat``,
   ``mx4_exponent`` -- the scalar conversions.
@@ -77,6 +79,8 @@ def _L():
         lib.oracle_combine_mxfp4.argtypes = common + [P, P] + dims
         lib.oracle_reduce_dense.argtypes = [P, I, P, P, P, P, F, F, P, P, I64, I64]
         lib.oracle_reduce_dense.restype = I
+        lib.oracle_dispatch.argtypes = [P, P, I64, I64, I, I, I, I64, P, P, P]
+        lib.oracle_dispatch.restype = I
         for f in ("oracle_routed_sum_f32", "oracle_combine",
                   "oracle_combine_residual_rmsnorm", "oracle_combine_mxfp8",
                   "oracle_combine_residual_rmsnorm_mxfp8", "oracle_combine_mxfp4"):
@@ -244,6 +248,25 @@ def reduce_dense(x, scales=None, tok=None, residual=None, gamma=None, eps=1e-6,
                                  float(0.0 if weight_bias is None else weight_bias),
                                  _ptr(out), _ptr(no), T, H))
     return out if residual is None else (out, no)
+
+
+def dispatch(x, topk_ids, E, ep, mtpr, payload=None, recv_counts=None):
+    """x bf16 bits [T, H]; topk_ids int32 [T, k] (-1 = dropped slot).
+    Returns (payload [ep, mtpr, H], src_info [T, k, 2], recv_counts [E]);
+    ``payload`` / ``recv_counts`` given are updated in place (rows no pair
+    is placed in keep their contents; counts accumulate)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    topk_ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if payload is None:
+        payload = np.zeros((ep, mtpr, H), dtype=np.uint16)
+    if recv_counts is None:
+        recv_counts = np.zeros(E, dtype=np.int32)
+    src = np.empty((T, k, 2), dtype=np.int32)
+    _rc(_L().oracle_dispatch(_ptr(x), _ptr(topk_ids), T, H, k, E, ep, mtpr,
+                             _ptr(payload), _ptr(src), _ptr(recv_counts)))
+    return payload, src, recv_counts
 
 
 def e2m1_rne_sat(x: float) -> int:

@@ -448,6 +448,53 @@ int oracle_reduce_dense(const uint16_t *x, int n_in, const float *scales,
     return 0;
 }
 
+/* Dispatch: the forward scatter the combine inverts
+ * (flashinfer.comm.moe_a2a_combine summary: the combine is the inverse of
+ * moe_a2a_dispatch; flashinfer.megamoe.nvfp4_mega_moe, Parameters num_tokens:
+ * slots routed to -1 carry nothing, and cumulative_local_expert_recv_stats:
+ * per-expert receive counts accumulated in place).
+ * Pairs (t, j) with topk_ids[t, j] >= 0 are taken expert by expert in
+ * ascending expert id, and within an expert in token-major, slot-minor order;
+ * expert e lives on rank e / (E / ep); the next free row of that rank is
+ * assigned. A row at or past mtpr drops the pair. For a placed pair:
+ *   src_info[t, j] = (rank, row), payload[rank, row, :] = x[t, :],
+ *   recv_counts[e] += 1 (if recv_counts is given);
+ * dropped pairs get (-1, -1). Unassigned payload rows are left untouched. */
+int oracle_dispatch(const uint16_t *x, const int32_t *topk_ids, int64_t T,
+                    int64_t H, int k, int E, int ep, int64_t mtpr,
+                    uint16_t *payload, int32_t *src_info, int32_t *recv_counts)
+{
+    if (T < 0 || H <= 0 || k < 1 || E < 1 || ep < 1 || E % ep || mtpr < 1)
+        return 2;
+    for (int64_t i = 0; i < T * k; ++i)
+        if (topk_ids[i] >= E || topk_ids[i] < -1)
+            return 1;
+    int64_t *next_row = calloc((size_t)ep, sizeof(int64_t));
+    if (!next_row)
+        return 2;
+    for (int64_t i = 0; i < T * k; ++i)
+        src_info[2 * i] = src_info[2 * i + 1] = -1;
+    int epr = E / ep;
+    for (int e = 0; e < E; ++e) {
+        int r = e / epr;
+        for (int64_t i = 0; i < T * k; ++i) {       /* i = t * k + j */
+            if (topk_ids[i] != e)
+                continue;
+            int64_t row = next_row[r]++;
+            if (row >= mtpr)
+                continue;                            /* over capacity */
+            src_info[2 * i] = r;
+            src_info[2 * i + 1] = (int32_t)row;
+            memcpy(payload + ((int64_t)r * mtpr + row) * H, x + (i / k) * H,
+                   (size_t)H * sizeof(uint16_t));
+            if (recv_counts)
+                recv_counts[e] += 1;
+        }
+    }
+    free(next_row);
+    return 0;
+}
+
 /* ---- threading ----------------------------------------------------------- */
 
 void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

@@ -692,3 +692,47 @@ def test_reduce_dense_special_cases():
     s = (rng.integers(1, 5, size=(7, 5)) / 4.0).astype(np.float32)
     exact = np.einsum("ti,ith->th", s.astype(np.float64), v)
     np.testing.assert_array_equal(oracle.reduce_dense(to_bf16_bits(v), s), to_bf16_bits(exact))
+
+
+# ------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("E,ep,k,cap,drop", [(16, 1, 1, None, 0.0), (32, 4, 4, None, 0.2),
+                                              (64, 8, 8, 40, 0.1), (8, 2, 3, 5, 0.0)])
+def test_dispatch_matches_generator_slot_map(E, ep, k, cap, drop):
+    """The oracle's expert-by-expert placement equals the generator's stable
+    argsort construction (two independent statements of the same order)."""
+    rng = np.random.default_rng(E + k)
+    T, H = 70, 16
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    dropped = rng.random((T, k)) < drop
+    src_g, loads = gen.dispatch_slots(topk, dropped, E, ep, cap)
+    mtpr = cap if cap else int(loads.max())
+    ids = np.where(dropped, -1, topk).astype(np.int32)
+    x = to_bf16_bits(rng.standard_normal((T, H)))
+    payload, src, counts = oracle.dispatch(x, ids, E, ep, mtpr)
+    np.testing.assert_array_equal(src, src_g)
+    v = src[..., 0] >= 0
+    tok = np.broadcast_to(np.arange(T)[:, None], (T, k))
+    np.testing.assert_array_equal(payload[src[..., 0][v], src[..., 1][v]], x[tok[v]])
+    assert counts.sum() == v.sum()
+    np.testing.assert_array_equal(counts, np.bincount(ids[v], minlength=E))
+    # rows of each rank are 0..n-1 with no gaps, and never past capacity
+    for r in range(ep):
+        rows = np.sort(src[..., 1][src[..., 0] == r])
+        np.testing.assert_array_equal(rows, np.arange(rows.size))
+        assert rows.size <= mtpr
+
+
+def test_dispatch_then_combine_is_identity_and_counts_accumulate():
+    rng = np.random.default_rng(4)
+    T, H, E, ep = 90, 32, 12, 3
+    ids = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    x = to_bf16_bits(rng.standard_normal((T, H)))
+    counts = np.zeros(E, np.int32)
+    fill = np.full((ep, 64, H), 0x7FC0, np.uint16)
+    payload, src, counts = oracle.dispatch(x, ids, E, ep, 64, payload=fill, recv_counts=counts)
+    np.testing.assert_array_equal(oracle.combine(payload, src, None), x)
+    _, _, counts2 = oracle.dispatch(x, ids, E, ep, 64, recv_counts=counts.copy())
+    np.testing.assert_array_equal(counts2, 2 * counts)
+    with pytest.raises(oracle.OracleError):
+        oracle.dispatch(x, np.full((T, 1), E, np.int32), E, ep, 64)
