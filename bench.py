@@ -30,7 +30,7 @@ PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 
 KIND = {"dsv3": "bf16", "skewed": "bf16", "tiny": "bf16", "rmsnorm": "rmsnorm",
         "mxfp8": "mxfp8", "rmsnorm_mxfp8": "rmsnorm_mxfp8", "mxfp4": "mxfp4",
-        "dense8": "dense"}
+        "dense8": "dense", "dispatch": "dispatch"}
 # workloads that reuse another workload's inputs
 INPUTS = {"rmsnorm_mxfp8": "rmsnorm", "mxfp4": "mxfp8"}
 DESCR = {
@@ -41,6 +41,7 @@ DESCR = {
     "tiny": "moe combine T=64 H=1024 top_k=2 E=8 ep=1, bf16 out",
     "mxfp4": "moe combine T=16384 H=7168 top_k=8 E=256 ep=8, MXFP4 e2m1 out + UE8M0/32 scales",
     "dense8": "local reduce of 8 partial sums [4096, 7168] bf16 (skip_a2a), bf16 out",
+    "dispatch": "moe dispatch (inverse scatter) T=4096 H=7168 top_k=8 E=256 ep=8 capacity 4224, bf16",
     "rmsnorm_mxfp8": "moe combine + residual + RMSNorm T=2048 H=7168 top_k=8 E=256 ep=8, weight_bias=1, normalised row as MXFP8 e4m3 + UE8M0/32",
 }
 
@@ -101,7 +102,17 @@ def main():
     def d16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    if kind == "dense":
+    if kind == "dispatch":
+        inp = gen.make_inputs(dict(gen.CONFIGS["dsv3"], H=8), args.seed)   # routing only
+        T, k, ep, mtpr, E = inp.T, inp.k, inp.ep, inp.mtpr, inp.meta["E"]
+        H = gen.CONFIGS["dsv3"]["H"]
+        xs = gen.normal_bf16((T, H), args.seed, 9)
+        kept = inp.meta["kept_slots"]
+        algo_bytes = T * H * 2 + kept * 2 * H + T * k * (4 + 8)
+        ws_bytes = mc.dispatch_workspace_size(T, k, E)
+        base = dict(payload=d16(xs), src=torch.from_numpy(inp.topk_ids).to(dev), w=None,
+                    shared=None)
+    elif kind == "dense":
         inp = gen.make_dense_inputs(args.workload, args.seed)
         T, H, k, ep, mtpr = inp.T, inp.H, inp.n_in, inp.n_in, inp.T
         algo_bytes = gen.dense_algorithmic_bytes(inp)
@@ -123,7 +134,11 @@ def main():
     sets = []
     for i in range(nsets):
         s = {kk: (None if v is None else (v if i == 0 else v.clone())) for kk, v in base.items()}
-        if kind in ("bf16", "dense"):
+        if kind == "dispatch":
+            s["pay"] = torch.empty((ep, mtpr, H), dtype=torch.bfloat16, device=dev)
+            s["si"] = torch.empty((T, k, 2), dtype=torch.int32, device=dev)
+            s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        elif kind in ("bf16", "dense"):
             s["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         elif kind == "rmsnorm":
             s["ro"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -147,7 +162,11 @@ def main():
     P = lambda t: None if t is None else t.data_ptr()
     calls = []
     for s in sets:
-        if kind == "dense":
+        if kind == "dispatch":
+            a = (P(s["payload"]), P(s["src"]), T, H, k, E, ep, mtpr, P(s["pay"]), P(s["si"]), None,
+                 P(s["ws"]), ws_bytes, sptr)
+            calls.append((L.moe_dispatch, a))
+        elif kind == "dense":
             a = (P(s["payload"]), k, None, None, P(s["out"]), T, H, sptr)
             calls.append((L.moe_reduce_dense, a))
         elif kind == "bf16":
@@ -236,7 +255,9 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        if kind == "dense":
+        if kind == "dispatch":
+            run = lambda: oracle.dispatch(xs, inp.topk_ids, E, ep, mtpr)
+        elif kind == "dense":
             run = lambda: oracle.reduce_dense(inp.x)
         elif kind == "bf16":
             run = lambda: oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared, checked=False)
@@ -274,8 +295,10 @@ def main():
                    "top_k": k, "ep_size": ep, "max_tokens_per_rank": mtpr,
                    "kept_slots": kept, "io_dtype": "bf16",
                    "seed": args.seed, "input_sets": nsets,
-                   "launch": mc.describe_launch({"bf16": 0, "dense": 0, "rmsnorm": 1, "mxfp8": 2,
-                                                 "rmsnorm_mxfp8": 3, "mxfp4": 4}[kind], T, H, k)},
+                   "launch": ("4 kernels: histogram, scan, rank, scatter (64 x 2 vectors)"
+                              if kind == "dispatch" else
+                              mc.describe_launch({"bf16": 0, "dense": 0, "rmsnorm": 1, "mxfp8": 2,
+                                                  "rmsnorm_mxfp8": 3, "mxfp4": 4}[kind], T, H, k))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": algo_bytes,

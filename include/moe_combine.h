@@ -64,6 +64,7 @@
 #ifndef MOE_COMBINE_H_
 #define MOE_COMBINE_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -245,6 +246,50 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(
     const void *token_input, const void *residual_in, const void *gamma,
     float eps, float weight_bias, void *residual_out, void *norm_out,
     int64_t num_tokens, int32_t hidden, void *stream);
+
+/*
+ * Dispatch: the forward scatter the combine inverts. It builds the payload
+ * and slot map that moe_combine consumes.
+ *
+ * Inputs:
+ *  - x: [num_tokens, hidden] bf16;
+ *  - topk_ids: [num_tokens, top_k] int32 expert ids in [0, num_experts).
+ *    -1 marks a dropped slot, and ids outside the range are treated as -1.
+ *  - ep_size: number of ranks. Expert e lives on rank e / (num_experts /
+ *    ep_size), so ep_size must divide num_experts (<= 4096).
+ *
+ * Placement: kept (token, slot) pairs are enumerated token-major and stably
+ * sorted by expert id. A pair's row is its position among its rank's pairs
+ * in that order. A row at or past max_tokens_per_rank drops the pair.
+ *
+ * For each placed pair, it writes:
+ *  - src_info[t, j] = (rank, row);
+ *  - payload[rank, row, :] = x[t, :];
+ *  - recv_counts[e] += 1 (counts accumulate in place; NULL skips them).
+ * Dropped pairs get (-1, -1). payload rows no pair is placed in are left
+ * untouched.
+ *
+ * workspace: caller-provided device memory of at least
+ * moe_dispatch_workspace_size(num_tokens, top_k, num_experts) bytes
+ * (4-byte aligned). Its contents on entry do not matter, and are
+ * overwritten. Calls that share a workspace must not overlap.
+ *
+ * Sources: flashinfer.comm.moe_a2a_combine (summary: the combine is the
+ * inverse of moe_a2a_dispatch); flashinfer.megamoe.nvfp4_mega_moe,
+ * Parameters num_tokens (rows routed to -1) and
+ * cumulative_local_expert_recv_stats (receive counts accumulated in place);
+ * Struct_ep_combine_skip_a2a, Args recv_count_ptrs and topk_ids.
+ */
+size_t moe_dispatch_workspace_size(int64_t num_tokens, int32_t top_k,
+                                   int32_t num_experts);
+
+moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids,
+                          int64_t num_tokens, int32_t hidden, int32_t top_k,
+                          int32_t num_experts, int32_t ep_size,
+                          int64_t max_tokens_per_rank, void *payload,
+                          int32_t *src_info, int32_t *recv_counts,
+                          void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /*
  * Describes the launch an entry point would make for these sizes, without

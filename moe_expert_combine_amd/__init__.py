@@ -27,6 +27,7 @@ from . import _build
 __all__ = ["moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
            "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
            "moe_reduce_dense", "moe_reduce_dense_residual_rmsnorm",
+           "moe_dispatch", "dispatch_workspace_size",
            "describe_launch", "abi_version", "lib", "library_path",
            "MoeCombineError"]
 
@@ -60,6 +61,10 @@ def _load():
     L.moe_reduce_dense.restype = ctypes.c_int
     L.moe_reduce_dense_residual_rmsnorm.argtypes = [P, I32, P, P, P, P, F, F, P, P, I64, I32, P]
     L.moe_reduce_dense_residual_rmsnorm.restype = ctypes.c_int
+    L.moe_dispatch_workspace_size.argtypes = [I64, I32, I32]
+    L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
+    L.moe_dispatch.argtypes = [P, P, I64, I32, I32, I32, I32, I64, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_dispatch.restype = ctypes.c_int
     for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
               "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4"):
         getattr(L, f).restype = ctypes.c_int
@@ -305,3 +310,46 @@ def moe_reduce_dense_residual_rmsnorm(inputs, scales, token_input, residual_in, 
         _ptr(inputs), n_in, _ptr(scales), _ptr(token_input), _ptr(residual_in), _ptr(gamma),
         float(eps), wb, _ptr(residual_out), _ptr(norm_out), T, H, _stream(dev)))
     return residual_out, norm_out
+
+
+def dispatch_workspace_size(num_tokens: int, top_k: int, num_experts: int) -> int:
+    return int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_experts))
+
+
+def moe_dispatch(x, topk_ids, num_experts, ep_size, max_tokens_per_rank, payload=None,
+                 src_info=None, recv_counts=None, workspace=None):
+    """Forward scatter: returns (payload bf16 [ep, mtpr, H], src_info int32
+    [T, k, 2]). recv_counts (int32 [E]) is accumulated in place if given.
+    A workspace is allocated with torch when none is passed."""
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(topk_ids, "topk_ids", torch.int32, dev, 2)
+    T, H = x.shape
+    if topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must be [T, top_k]")
+    k = topk_ids.shape[1]
+    if payload is None:
+        payload = torch.zeros((ep_size, max_tokens_per_rank, H), dtype=torch.bfloat16, device=dev)
+    _need(payload, "payload", torch.bfloat16, dev, 3)
+    if tuple(payload.shape) != (ep_size, max_tokens_per_rank, H):
+        raise ValueError(f"payload must be [{ep_size}, {max_tokens_per_rank}, {H}]")
+    if src_info is None:
+        src_info = torch.empty((T, k, 2), dtype=torch.int32, device=dev)
+    _need(src_info, "src_info", torch.int32, dev, 3)
+    if tuple(src_info.shape) != (T, k, 2):
+        raise ValueError(f"src_info must be [{T}, {k}, 2]")
+    if recv_counts is not None:
+        _need(recv_counts, "recv_counts", torch.int32, dev, 1)
+        if recv_counts.shape[0] != num_experts:
+            raise ValueError(f"recv_counts must be [{num_experts}]")
+    need = dispatch_workspace_size(T, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev, 1)
+    _check("moe_dispatch", lib().moe_dispatch(
+        _ptr(x), _ptr(topk_ids), T, H, k, num_experts, ep_size, max_tokens_per_rank,
+        _ptr(payload), _ptr(src_info), _ptr(recv_counts), _ptr(workspace), workspace.numel(),
+        _stream(dev)))
+    return payload, src_info

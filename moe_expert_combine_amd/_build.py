@@ -13,6 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_combine.so")
 SOURCES = [os.path.join(CSRC, "moe_combine.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, "combine_kernels.h"),
+                  os.path.join(CSRC, "dispatch_kernels.h"),
                   os.path.join(ROOT, "include", "moe_combine.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

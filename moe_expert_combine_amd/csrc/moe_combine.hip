@@ -14,6 +14,7 @@
 
 #include "moe_combine.h"
 #include "combine_kernels.h"
+#include "dispatch_kernels.h"
 
 namespace {
 
@@ -383,6 +384,69 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(const void *inputs, int32_t n_in,
     a.eps = eps;
     a.wb = weight_bias;
     return launch<moe::EPI_RMSNORM>(p, a, stream);
+}
+
+static int64_t dispatch_chunks(int64_t T, int32_t k) { return (T * k + moe::kChunk - 1) / moe::kChunk; }
+
+size_t moe_dispatch_workspace_size(int64_t num_tokens, int32_t top_k, int32_t num_experts) {
+    if (num_tokens < 0 || top_k < 1 || num_experts < 1) return 0;
+    const int64_t n = (dispatch_chunks(num_tokens, top_k) + 1) * (int64_t)num_experts * 4;
+    return (size_t)((n + 255) / 256 * 256);
+}
+
+moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_tokens, int32_t hidden,
+                          int32_t top_k, int32_t num_experts, int32_t ep_size, int64_t max_tokens_per_rank,
+                          void *payload, int32_t *src_info, int32_t *recv_counts, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (num_tokens < 0 || num_tokens > 0x7FFFFFFFLL)
+        return fail(MOE_ERR_INVALID_ARG, "num_tokens must be in [0, 2^31)");
+    if (hidden <= 0 || hidden % 8) return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", hidden);
+    if (top_k < 1 || top_k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, %d] (got %d)", kMaxTopK, top_k);
+    if (num_experts < 1 || num_experts > moe::kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "num_experts must be in [1, %d] (got %d)", moe::kMaxExperts, num_experts);
+    if (ep_size < 1 || num_experts % ep_size)
+        return fail(MOE_ERR_INVALID_ARG, "ep_size must divide num_experts (got %d, %d)", ep_size, num_experts);
+    if (max_tokens_per_rank < 1 || max_tokens_per_rank > 0x7FFFFFFFLL)
+        return fail(MOE_ERR_INVALID_ARG, "max_tokens_per_rank must be in [1, 2^31)");
+    if (num_tokens * (int64_t)top_k > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens * top_k must be < 2^31");
+    if (num_tokens == 0) return ok();
+    if (!x || !topk_ids || !payload || !src_info || !workspace)
+        return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, payload, src_info and workspace are required");
+    if (!aligned(x, 16) || !aligned(payload, 16) || !aligned(src_info, 8) || !aligned(topk_ids, 4) ||
+        (recv_counts && !aligned(recv_counts, 4)) || !aligned(workspace, 4))
+        return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x, payload 16 B; src_info 8 B; others 4 B)");
+    if (workspace_bytes < moe_dispatch_workspace_size(num_tokens, top_k, num_experts))
+        return fail(MOE_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes,
+                    moe_dispatch_workspace_size(num_tokens, top_k, num_experts));
+    if (payload == x || (const void *)src_info == (const void *)topk_ids)
+        return fail(MOE_ERR_INVALID_ARG, "outputs must not alias inputs");
+    moe::DispatchArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = static_cast<const uint16_t *>(x);
+    a.ids = topk_ids;
+    a.payload = static_cast<uint16_t *>(payload);
+    a.src_info = src_info;
+    a.recv_counts = recv_counts;
+    a.pairs = num_tokens * top_k;
+    a.nchunks = (int)dispatch_chunks(num_tokens, top_k);
+    a.hist = static_cast<int32_t *>(workspace);
+    a.base = a.hist + (int64_t)a.nchunks * num_experts;
+    a.mtpr = max_tokens_per_rank;
+    a.T = (int)num_tokens;
+    a.H = hidden;
+    a.k = top_k;
+    a.E = num_experts;
+    a.epr = num_experts / ep_size;
+    a.hchunks = (hidden / 8 + 127) / 128;
+    if ((int64_t)a.T * a.hchunks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(moe::dispatch_hist, dim3(a.nchunks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(moe::dispatch_scan, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(moe::dispatch_rank, dim3(a.nchunks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(moe::dispatch_scatter<2>, dim3((unsigned)((int64_t)a.T * a.hchunks)), dim3(64), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,

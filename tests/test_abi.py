@@ -28,6 +28,7 @@ def test_header_declares_the_entry_points():
     for n in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
               "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
               "moe_reduce_dense", "moe_reduce_dense_residual_rmsnorm",
+              "moe_dispatch", "moe_dispatch_workspace_size",
               "moe_combine_describe_launch", "moe_combine_abi_version",
               "moe_combine_status_string", "moe_combine_last_error"):
         assert n in names
@@ -142,6 +143,27 @@ def test_reduce_dense_argument_errors():
     assert g(no=5 * A) == INVALID
     assert g(res=None) == INVALID
     assert g(no=3 * A) == INVALID
+
+
+def test_dispatch_argument_errors_and_workspace_size():
+    L = mc.lib()
+    assert mc.dispatch_workspace_size(4096, 8, 256) == (32 + 1) * 256 * 4
+    assert mc.dispatch_workspace_size(1, 1, 8) == 256          # rounded to 256 B
+    assert mc.dispatch_workspace_size(-1, 8, 8) == 0
+    ws = mc.dispatch_workspace_size(4, 2, 8)
+
+    def f(x=A, ids=A, T=4, H=64, k=2, E=8, ep=2, mtpr=8, pay=2 * A, src=3 * A, cnt=None, w=4 * A, wb=ws):
+        return L.moe_dispatch(x, ids, T, H, k, E, ep, mtpr, pay, src, cnt, w, wb, None)
+    assert f(E=9, ep=2) == INVALID    # ep must divide E
+    assert f(E=5000) == INVALID
+    assert f(k=0) == INVALID
+    assert f(H=12) == INVALID
+    assert f(mtpr=0) == INVALID
+    assert f(w=None) == INVALID
+    assert f(wb=ws - 4) == INVALID and "workspace too small" in L.moe_combine_last_error().decode()
+    assert f(src=3 * A + 4) == INVALID
+    assert f(pay=A) == INVALID        # payload aliases x
+    assert f(T=0, x=None, ids=None, pay=None, src=None, w=None) == OK
 
 
 def test_rmsnorm_mxfp8_argument_errors():

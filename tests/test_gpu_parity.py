@@ -520,3 +520,80 @@ def test_full_size_dense8():
     d = gen.make_dense_inputs("dense8", 0)
     out = mc.moe_reduce_dense(dev16(d.x))
     check_bf16(host16(out), oracle.reduce_dense(d.x), 1e-3, "dense8")
+
+
+# ------------------------------------------------------------- dispatch
+
+def _dispatch_case(T, H, k, E, ep, cap, drop, seed, bad_ids=False):
+    rng = np.random.default_rng(seed)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    ids[rng.random((T, k)) < drop] = -1
+    if bad_ids:
+        ids[rng.random((T, k)) < 0.05] = E + 3          # out of range -> dropped
+    x = to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    clean = np.where((ids >= 0) & (ids < E), ids, -1).astype(np.int32)
+    if cap is None:
+        kept = clean[clean >= 0]
+        cap = max(1, int(np.bincount(kept // (E // ep), minlength=ep).max()) if kept.size else 1)
+    return x, ids, clean, cap
+
+
+@pytest.mark.parametrize("T,H,k,E,ep,cap,drop,bad", [
+    (1, 8, 1, 1, 1, None, 0.0, False),
+    (37, 264, 3, 12, 3, None, 0.1, False),
+    (300, 1024, 8, 64, 8, 40, 0.0, False),         # capacity drops
+    (1500, 512, 4, 256, 4, None, 0.2, True),       # > one chunk, bad ids
+    (2048, 2048, 8, 4096, 8, None, 0.0, False),    # maximum expert count
+    (513, 96, 32, 32, 1, 200, 0.0, False),         # top_k = 32, tight capacity
+])
+def test_dispatch_matches_oracle(T, H, k, E, ep, cap, drop, bad):
+    x, ids, clean, cap = _dispatch_case(T, H, k, E, ep, cap, drop, seed=T + k, bad_ids=bad)
+    poison = np.full((ep, cap, H), 0xFFFF, np.uint16)
+    counts0 = np.arange(E, dtype=np.int32) % 7                 # accumulates onto this
+    rp, rs, rc = oracle.dispatch(x, clean, E, ep, cap, payload=poison.copy(), recv_counts=counts0.copy())
+    pay = dev16(poison)
+    cnt = torch.from_numpy(counts0.copy()).to(DEV)
+    pay, src = mc.moe_dispatch(dev16(x), torch.from_numpy(ids).to(DEV), E, ep, cap,
+                               payload=pay, recv_counts=cnt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(src.cpu().numpy(), rs)
+    np.testing.assert_array_equal(host16(pay), rp)               # placed rows and untouched ones
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+
+
+def test_dispatch_identity_combine_round_trip_on_gpu():
+    """GPU dispatch -> identity experts -> GPU combine gives the oracle's bits
+    for the same pipeline, and bf16(x * sum of kept weights) within 1 step."""
+    inp = gen.make_inputs(dict(T=512, H=2048, E=64, ep=8, k=8, drop_frac=0.1), seed=3)
+    rng = np.random.default_rng(0)
+    x = to_bf16_bits(rng.standard_normal((inp.T, inp.H)).astype(np.float32))
+    ids = inp.topk_ids.copy()
+    ids[inp.src_info[..., 0] < 0] = -1
+    cap = inp.mtpr
+    pay, src = mc.moe_dispatch(dev16(x), torch.from_numpy(ids).to(DEV), 64, 8, cap)
+    w = torch.from_numpy(inp.weights).to(DEV)
+    out = host16(mc.moe_combine(pay, src, w))
+    rp, rs, _ = oracle.dispatch(x, ids, 64, 8, cap)
+    np.testing.assert_array_equal(out, oracle.combine(rp, rs, inp.weights))
+    f = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wsum = np.where(rs[..., 0] >= 0, inp.weights, 0).astype(np.float64).sum(axis=1)
+    assert ulp_dist_bf16(out, to_bf16_bits(f * wsum[:, None])).max() <= 1
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["dsv3", "mxfp8"])
+def test_full_size_dispatch(name):
+    inp = gen.make_inputs(dict(gen.CONFIGS[name], H=8), seed=0)   # routing only
+    T, H, E = inp.T, gen.CONFIGS[name]["H"], inp.meta["E"]
+    rng = np.random.default_rng(1)
+    x = to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    rp, rs, rc = oracle.dispatch(x, inp.topk_ids, E, inp.ep, inp.mtpr)
+    cnt = torch.zeros(E, dtype=torch.int32, device=DEV)
+    pay, src = mc.moe_dispatch(dev16(x), torch.from_numpy(inp.topk_ids).to(DEV), E, inp.ep,
+                               inp.mtpr, recv_counts=cnt)
+    np.testing.assert_array_equal(src.cpu().numpy(), rs)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+    np.testing.assert_array_equal(src.cpu().numpy(), inp.src_info)   # generator's map too
+    v = rs[..., 0] >= 0
+    np.testing.assert_array_equal(host16(pay)[rs[..., 0][v], rs[..., 1][v]],
+                                  rp[rs[..., 0][v], rs[..., 1][v]])
