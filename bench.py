@@ -109,7 +109,7 @@ def main():
         xs = gen.normal_bf16((T, H), args.seed, 9)
         kept = inp.meta["kept_slots"]
         algo_bytes = T * H * 2 + kept * 2 * H + T * k * (4 + 8)
-        ws_bytes = mc.dispatch_workspace_size(T, k, E)
+        ws_bytes = mc.dispatch_workspace_size(T, k, E, ep, mtpr)
         base = dict(payload=d16(xs), src=torch.from_numpy(inp.topk_ids).to(dev), w=None,
                     shared=None)
     elif kind == "dense":
@@ -295,7 +295,7 @@ def main():
                    "top_k": k, "ep_size": ep, "max_tokens_per_rank": mtpr,
                    "kept_slots": kept, "io_dtype": "bf16",
                    "seed": args.seed, "input_sets": nsets,
-                   "launch": ("4 kernels: histogram, scan, rank, scatter (64 x 2 vectors)"
+                   "launch": ("4 kernels: histogram, scan, rank, token-order row scatter (64 x 2 vectors)"
                               if kind == "dispatch" else
                               mc.describe_launch({"bf16": 0, "dense": 0, "rmsnorm": 1, "mxfp8": 2,
                                                   "rmsnorm_mxfp8": 3, "mxfp4": 4}[kind], T, H, k))},

@@ -270,9 +270,10 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(
  * untouched.
  *
  * workspace: caller-provided device memory of at least
- * moe_dispatch_workspace_size(num_tokens, top_k, num_experts) bytes
- * (4-byte aligned). Its contents on entry do not matter, and are
- * overwritten. Calls that share a workspace must not overlap.
+ * moe_dispatch_workspace_size(num_tokens, top_k, num_experts, ep_size,
+ * max_tokens_per_rank) bytes (4-byte aligned). Its contents on entry do not
+ * matter, and are overwritten. Calls that share a workspace must not
+ * overlap.
  *
  * Sources: flashinfer.comm.moe_a2a_combine (summary: the combine is the
  * inverse of moe_a2a_dispatch); flashinfer.megamoe.nvfp4_mega_moe,
@@ -281,7 +282,8 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(
  * Struct_ep_combine_skip_a2a, Args recv_count_ptrs and topk_ids.
  */
 size_t moe_dispatch_workspace_size(int64_t num_tokens, int32_t top_k,
-                                   int32_t num_experts);
+                                   int32_t num_experts, int32_t ep_size,
+                                   int64_t max_tokens_per_rank);
 
 moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids,
                           int64_t num_tokens, int32_t hidden, int32_t top_k,

@@ -61,7 +61,7 @@ def _load():
     L.moe_reduce_dense.restype = ctypes.c_int
     L.moe_reduce_dense_residual_rmsnorm.argtypes = [P, I32, P, P, P, P, F, F, P, P, I64, I32, P]
     L.moe_reduce_dense_residual_rmsnorm.restype = ctypes.c_int
-    L.moe_dispatch_workspace_size.argtypes = [I64, I32, I32]
+    L.moe_dispatch_workspace_size.argtypes = [I64, I32, I32, I32, I64]
     L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
     L.moe_dispatch.argtypes = [P, P, I64, I32, I32, I32, I32, I64, P, P, P, P, ctypes.c_size_t, P]
     L.moe_dispatch.restype = ctypes.c_int
@@ -312,8 +312,10 @@ def moe_reduce_dense_residual_rmsnorm(inputs, scales, token_input, residual_in, 
     return residual_out, norm_out
 
 
-def dispatch_workspace_size(num_tokens: int, top_k: int, num_experts: int) -> int:
-    return int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_experts))
+def dispatch_workspace_size(num_tokens: int, top_k: int, num_experts: int, ep_size: int,
+                            max_tokens_per_rank: int) -> int:
+    return int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_experts, ep_size,
+                                                 max_tokens_per_rank))
 
 
 def moe_dispatch(x, topk_ids, num_experts, ep_size, max_tokens_per_rank, payload=None,
@@ -344,7 +346,7 @@ def moe_dispatch(x, topk_ids, num_experts, ep_size, max_tokens_per_rank, payload
         _need(recv_counts, "recv_counts", torch.int32, dev, 1)
         if recv_counts.shape[0] != num_experts:
             raise ValueError(f"recv_counts must be [{num_experts}]")
-    need = dispatch_workspace_size(T, k, num_experts)
+    need = dispatch_workspace_size(T, k, num_experts, ep_size, max_tokens_per_rank)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev, 1)

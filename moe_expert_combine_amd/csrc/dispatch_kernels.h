@@ -21,7 +21,10 @@
 //                      running per-expert row in LDS carries it across
 //                      groups; writes src_info;
 //   4. dispatch_scatter: workgroup per (token, hidden chunk) reads the token's
-//                      row once and stores it to each of its placed rows.
+//                      row once and stores it to each of its placed rows (on
+//                      MI355X this beats copying in payload order, whose
+//                      randomly ordered re-reads of token rows cost more than
+//                      the streamed writes save).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,7 +32,7 @@
 
 namespace moe {
 
-constexpr int kChunk = 1024;          // pairs per histogram / rank chunk
+constexpr int kChunk = 256;           // pairs per histogram / rank chunk
 constexpr int kMaxExperts = 4096;     // LDS counters and 13-bit id match
 constexpr int kIdBits = 13;           // ids 0..E-1 plus the sentinel E < 8192
 
@@ -65,16 +68,22 @@ __global__ __launch_bounds__(256) void dispatch_hist(DispatchArgs a) {
     for (int e = threadIdx.x; e < a.E; e += blockDim.x) h[e] = cnt[e];
 }
 
-// One workgroup. Thread e (strided) owns expert e.
+// One workgroup. Thread e (strided) owns expert e; chunk counts are read 16
+// at a time before their prefixes are written back, so the loads overlap.
 __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs a) {
     __shared__ int total[kMaxExperts];
     for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
         int run = 0;
-        for (int c = 0; c < a.nchunks; ++c) {
-            int32_t *h = a.hist + (int64_t)c * a.E + e;
-            const int v = *h;
-            *h = run;
-            run += v;
+        for (int c0 = 0; c0 < a.nchunks; c0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = (c0 + i < a.nchunks) ? a.hist[(int64_t)(c0 + i) * a.E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (c0 + i < a.nchunks) a.hist[(int64_t)(c0 + i) * a.E + e] = run;
+                run += v[i];
+            }
         }
         total[e] = run;
     }
@@ -103,10 +112,17 @@ __global__ __launch_bounds__(64) void dispatch_rank(DispatchArgs a) {
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below
     const uint64_t gt = (lane == 63) ? 0ull : (~0ull << (lane + 1));   // lanes above
     const int64_t p0 = (int64_t)c * kChunk;
-    for (int g = 0; g < kChunk; g += 64) {
-        const int64_t p = p0 + g + lane;
+    int ids[kChunk / 64];                                // the chunk's ids, prefetched
+#pragma unroll
+    for (int i = 0; i < kChunk / 64; ++i) {
+        const int64_t p = p0 + i * 64 + lane;
+        ids[i] = p < a.pairs ? a.ids[p] : -1;
+    }
+#pragma unroll
+    for (int gi = 0; gi < kChunk / 64; ++gi) {
+        const int64_t p = p0 + gi * 64 + lane;
         const bool in = p < a.pairs;
-        int id = in ? clean_id(a.ids[p], a.E) : -1;
+        int id = in ? clean_id(ids[gi], a.E) : -1;
         const int key = id >= 0 ? id : a.E;             // sentinel for dropped
         // lanes holding the same key: intersect the ballots of all key bits
         uint64_t same = ~0ull;

@@ -388,8 +388,11 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(const void *inputs, int32_t n_in,
 
 static int64_t dispatch_chunks(int64_t T, int32_t k) { return (T * k + moe::kChunk - 1) / moe::kChunk; }
 
-size_t moe_dispatch_workspace_size(int64_t num_tokens, int32_t top_k, int32_t num_experts) {
-    if (num_tokens < 0 || top_k < 1 || num_experts < 1) return 0;
+size_t moe_dispatch_workspace_size(int64_t num_tokens, int32_t top_k, int32_t num_experts, int32_t ep_size,
+                                   int64_t max_tokens_per_rank) {
+    if (num_tokens < 0 || top_k < 1 || num_experts < 1 || ep_size < 1 || max_tokens_per_rank < 1) return 0;
+    // hist [nchunks, E] + base [E], int32 (ep_size and capacity are part of
+    // the signature so that the layout may depend on them)
     const int64_t n = (dispatch_chunks(num_tokens, top_k) + 1) * (int64_t)num_experts * 4;
     return (size_t)((n + 255) / 256 * 256);
 }
@@ -415,9 +418,9 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_to
     if (!aligned(x, 16) || !aligned(payload, 16) || !aligned(src_info, 8) || !aligned(topk_ids, 4) ||
         (recv_counts && !aligned(recv_counts, 4)) || !aligned(workspace, 4))
         return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x, payload 16 B; src_info 8 B; others 4 B)");
-    if (workspace_bytes < moe_dispatch_workspace_size(num_tokens, top_k, num_experts))
-        return fail(MOE_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes,
-                    moe_dispatch_workspace_size(num_tokens, top_k, num_experts));
+    const size_t need = moe_dispatch_workspace_size(num_tokens, top_k, num_experts, ep_size, max_tokens_per_rank);
+    if (workspace_bytes < need)
+        return fail(MOE_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
     if (payload == x || (const void *)src_info == (const void *)topk_ids)
         return fail(MOE_ERR_INVALID_ARG, "outputs must not alias inputs");
     moe::DispatchArgs a;

@@ -147,10 +147,11 @@ def test_reduce_dense_argument_errors():
 
 def test_dispatch_argument_errors_and_workspace_size():
     L = mc.lib()
-    assert mc.dispatch_workspace_size(4096, 8, 256) == (32 + 1) * 256 * 4
-    assert mc.dispatch_workspace_size(1, 1, 8) == 256          # rounded to 256 B
-    assert mc.dispatch_workspace_size(-1, 8, 8) == 0
-    ws = mc.dispatch_workspace_size(4, 2, 8)
+    n = (4096 * 8 // 256 + 1) * 256 * 4
+    assert mc.dispatch_workspace_size(4096, 8, 256, 8, 4224) == (n + 255) // 256 * 256
+    assert mc.dispatch_workspace_size(1, 1, 8, 1, 1) == 256     # rounded to 256 B
+    assert mc.dispatch_workspace_size(-1, 8, 8, 1, 1) == 0
+    ws = mc.dispatch_workspace_size(4, 2, 8, 2, 8)
 
     def f(x=A, ids=A, T=4, H=64, k=2, E=8, ep=2, mtpr=8, pay=2 * A, src=3 * A, cnt=None, w=4 * A, wb=ws):
         return L.moe_dispatch(x, ids, T, H, k, E, ep, mtpr, pay, src, cnt, w, wb, None)
