@@ -24,7 +24,7 @@
 //                      row once and stores it to each of its placed rows (on
 //                      MI355X this beats copying in payload order, whose
 //                      randomly ordered re-reads of token rows cost more than
-//                      the streamed writes save).
+//                      sequential writes save).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -150,7 +150,9 @@ __global__ __launch_bounds__(64) void dispatch_rank(DispatchArgs a) {
 typedef unsigned int du32x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup per (token, chunk of 64 * V 16-byte vectors); the token row is
-// read once and written to each placed row.
+// read once and written to each placed row. The scattered row writes go
+// through L2 (write-back): on MI355X that is about 3% faster here than
+// non-temporal stores, unlike the combine's sequential output rows.
 template <int V>
 __global__ __launch_bounds__(64) void dispatch_scatter(DispatchArgs a) {
     const int t = blockIdx.x / a.hchunks;
@@ -163,8 +165,7 @@ __global__ __launch_bounds__(64) void dispatch_scatter(DispatchArgs a) {
     for (int u = 0; u < V; ++u) {
         vi[u] = (c * V + u) * 64 + threadIdx.x;
         ok[u] = vi[u] < nvec;
-        if (ok[u]) v[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const du32x4 *>(a.x + (int64_t)t * a.H + (int64_t)vi[u] * 8));
+        if (ok[u]) v[u] = *reinterpret_cast<const du32x4 *>(a.x + (int64_t)t * a.H + (int64_t)vi[u] * 8);
     }
     const int2 *si = reinterpret_cast<const int2 *>(a.src_info) + (int64_t)t * a.k;
     for (int j = 0; j < a.k; ++j) {
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(64) void dispatch_scatter(DispatchArgs a) {
         uint16_t *dst = a.payload + ((int64_t)rr.x * a.mtpr + rr.y) * a.H;
 #pragma unroll
         for (int u = 0; u < V; ++u)
-            if (ok[u]) __builtin_nontemporal_store(v[u], reinterpret_cast<du32x4 *>(dst + (int64_t)vi[u] * 8));
+            if (ok[u]) *reinterpret_cast<du32x4 *>(dst + (int64_t)vi[u] * 8) = v[u];
     }
 }
 
