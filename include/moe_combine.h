@@ -301,9 +301,10 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids,
  * On success, writes a NUL-terminated text into buf, such as
  * "threads=128 vec_per_thread=1 chunks=7 blocks=28672 slot_tile=8 masked=0",
  * and returns MOE_OK. It validates the sizes like the entry point does.
- * The environment variable MOE_COMBINE_TILE="<threads>x<vectors>"
+ * The environment variable MOE_COMBINE_TILE="<threads>x<vectors>[x<kt>]"
  * overrides the threads per block and the 16-byte vectors per thread of
- * every entry point.
+ * every combine entry point. kt, one of 2, 4 or 8, caps the slot tile, the
+ * number of slots whose rows are loaded together.
  */
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens,
                                          int32_t hidden, int32_t top_k,

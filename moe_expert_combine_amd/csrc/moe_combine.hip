@@ -50,24 +50,28 @@ struct Plan {
     int64_t blocks;
 };
 
-// Optional override "<threads>x<vectors>" for tuning sweeps.
-bool tile_override(int *threads, int *vec) {
+// Optional override "<threads>x<vectors>[x<slot tile>]" for tuning sweeps.
+bool tile_override(int *threads, int *vec, int *kt) {
     const char *s = getenv("MOE_COMBINE_TILE");
     if (!s || !*s || !strcmp(s, "auto")) return false;
-    int t = 0, v = 0;
-    if (sscanf(s, "%dx%d", &t, &v) != 2) return false;
+    int t = 0, v = 0, k = 0;
+    const int n = sscanf(s, "%dx%dx%d", &t, &v, &k);
+    if (n < 2) return false;
     if (t < 64 || t > kMaxThreads || t % 64 || !(v == 1 || v == 2 || v == 4 || v == 8)) return false;
     if (v >= 4 && t > 512) return false;   // register budget of the V >= 4 kernels
+    if (n == 3 && !(k == 2 || k == 4 || k == 8)) return false;
     *threads = t;
     *vec = v;
+    *kt = n == 3 ? k : 0;
     return true;
 }
 
 moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
     const int nvec = H / 8;
     p->kt = k <= 2 ? 2 : (k <= 4 ? 4 : 8);
-    int threads = 0, vec = 0;
-    const bool forced = tile_override(&threads, &vec);
+    int threads = 0, vec = 0, kt = 0;
+    const bool forced = tile_override(&threads, &vec, &kt);
+    if (forced && kt && kt < p->kt) p->kt = kt;
     if (kind == moe::EPI_RMSNORM || kind == moe::EPI_RMSNORM_MXFP8) {
         // The row reduction needs the whole token in one workgroup.
         if (!forced) {
@@ -98,6 +102,14 @@ moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
     p->vec = vec;
     // at most 16 loads in flight per lane: shrink the slot tile for wide rows
     while (p->kt * vec > 16) p->kt /= 2;
+    // The RMSNorm epilogues run after a workgroup barrier; a smaller slot
+    // tile frees registers for more resident workgroups, which hides that
+    // serial tail (measured on MI355X at T=2048, H=7168: slot tile 4 for
+    // RMSNorm, 2 when the normalised row is also quantised).
+    if (!(forced && kt)) {
+        if (kind == moe::EPI_RMSNORM && p->kt > 4) p->kt = 4;
+        if (kind == moe::EPI_RMSNORM_MXFP8 && p->kt > 2) p->kt = 2;
+    }
     p->masked = (int64_t)p->chunks * threads * vec != nvec;
     p->blocks = T * (int64_t)p->chunks;
     if (p->blocks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large (%lld workgroups)", (long long)p->blocks);

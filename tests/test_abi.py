@@ -193,8 +193,8 @@ def test_describe_launch_shapes():
     d = mc.describe_launch(0, 100, 4096, 8)
     assert "chunks=4" in d and "masked=0" in d
     d = mc.describe_launch(1, 2048, 7168, 8)
-    assert "threads=448 vec_per_thread=2 chunks=1" in d
-    assert d == mc.describe_launch(3, 2048, 7168, 8)
+    assert "threads=448 vec_per_thread=2 chunks=1 blocks=2048 slot_tile=4" in d
+    assert "threads=448 vec_per_thread=2 chunks=1 blocks=2048 slot_tile=2" in mc.describe_launch(3, 2048, 7168, 8)
     with pytest.raises(mc.MoeCombineError):
         mc.describe_launch(3, 4, 48, 2)
     d = mc.describe_launch(2, 16384, 7168, 8)
@@ -219,6 +219,13 @@ def test_tile_override_env(monkeypatch):
     assert "slot_tile=4" in mc.describe_launch(0, 10, 7168, 8)
     monkeypatch.setenv("MOE_COMBINE_TILE", "1024x4")  # over the V>=4 budget -> ignored
     assert "threads=64 vec_per_thread=2" in mc.describe_launch(0, 10, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "448x2x4")
+    assert "threads=448 vec_per_thread=2 chunks=1 blocks=20 slot_tile=4" in mc.describe_launch(1, 20, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "448x2x8")  # explicit slot tile wins
+    assert "slot_tile=8" in mc.describe_launch(1, 20, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "448x2x3")  # bad slot tile -> ignored
+    assert "threads=448 vec_per_thread=2" in mc.describe_launch(1, 20, 7168, 8)
+    assert "slot_tile=4" in mc.describe_launch(1, 20, 7168, 8)
     monkeypatch.setenv("MOE_COMBINE_TILE", "100x3")   # invalid -> ignored
     assert "threads=64 vec_per_thread=2" in mc.describe_launch(0, 10, 7168, 8)
 
