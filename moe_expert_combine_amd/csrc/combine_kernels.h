@@ -204,52 +204,15 @@ __device__ __forceinline__ void mx4_quantize_store(const float (&x)[V][8], const
     }
 }
 
-// Register budget: KT * V 16-byte loads are in flight per lane (KT * V <= 16,
-// 64 VGPRs) plus 8 * V fp32 sums and up to 3 * 4 * V VGPRs of prefetched
-// shared / residual / gamma vectors, so V >= 4 needs more than the 128 VGPRs a
-// 1024-thread workgroup allows and is launched with at most 512 threads.
-template <int V>
-constexpr int max_threads_for() { return V >= 4 ? 512 : 1024; }
-
-// KT: slot tile; V: 16-byte vectors per lane; EPI: output kind; MASK: the
-// chunk may run past hidden / 8 vectors; SH: a shared-expert row is added.
-template <int KT, int V, int EPI, bool MASK, bool SH>
-__global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArgs a) {
-    __shared__ double lds_red[16];
-    const int nt = blockDim.x;
-    const int tid = threadIdx.x;
-    const int t = blockIdx.x / a.chunks;
-    const int c = blockIdx.x - t * a.chunks;
-    const int64_t row_off = (int64_t)t * a.H;          // output/shared row
-
-    int vi[V];
-    bool ok[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        vi[v] = (c * V + v) * nt + tid;
-        ok[v] = !MASK || vi[v] < a.nvec;
-    }
-
-    float acc[V][8];
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
-
-    // Rows that do not depend on the slot map are requested first, so their
-    // latency overlaps the gathers instead of following them.
-    u32x4 shv[V], resv[V], gmv[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        shv[v] = resv[v] = gmv[v] = (u32x4){0u, 0u, 0u, 0u};
-        if (!ok[v]) continue;
-        if constexpr (SH) shv[v] = ld_stream(a.shared + row_off + (int64_t)vi[v] * 8);
-        if constexpr (EPI == EPI_RMSNORM || EPI == EPI_RMSNORM_MXFP8) {
-            resv[v] = ld_stream(a.residual + row_off + (int64_t)vi[v] * 8);
-            if constexpr (V <= 4) gmv[v] = ld_cached(a.gamma + (int64_t)vi[v] * 8);
-        }
-    }
-
+// The routed sum of one (token, chunk): for each group of KT slots, load the
+// slot map and weights (wave-uniform), issue every row load of the group,
+// then take one fp32 fused multiply-add per kept slot in ascending slot
+// order (Struct_ep_combine_skip_a2a, execute: the weighted sum of the routed
+// expert outputs). A null slot map means dense inputs [k, T, H]: slot j of
+// token t is row t of input j.
+template <int KT, int V>
+__device__ __forceinline__ void gather_sum(const KernelArgs &a, int t, const int (&vi)[V],
+                                           const bool (&ok)[V], float (&acc)[V][8]) {
     const int32_t *__restrict__ si = a.src_info ? a.src_info + (int64_t)t * a.k * 2 : nullptr;
     const float *__restrict__ wt = a.weights ? a.weights + (int64_t)t * a.k : nullptr;
 
@@ -316,6 +279,56 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
                     acc[v][e] = __builtin_fmaf(w[jj], bf16_elem(x[jj][v], e), acc[v][e]);
         }
     }
+
+}
+
+// Register budget: KT * V 16-byte loads are in flight per lane (KT * V <= 16,
+// 64 VGPRs) plus 8 * V fp32 sums and up to 3 * 4 * V VGPRs of prefetched
+// shared / residual / gamma vectors, so V >= 4 needs more than the 128 VGPRs a
+// 1024-thread workgroup allows and is launched with at most 512 threads.
+template <int V>
+constexpr int max_threads_for() { return V >= 4 ? 512 : 1024; }
+
+// KT: slot tile; V: 16-byte vectors per lane; EPI: output kind; MASK: the
+// chunk may run past hidden / 8 vectors; SH: a shared-expert row is added.
+template <int KT, int V, int EPI, bool MASK, bool SH>
+__global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArgs a) {
+    __shared__ double lds_red[16];
+    const int nt = blockDim.x;
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x / a.chunks;
+    const int c = blockIdx.x - t * a.chunks;
+    const int64_t row_off = (int64_t)t * a.H;          // output/shared row
+
+    int vi[V];
+    bool ok[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        vi[v] = (c * V + v) * nt + tid;
+        ok[v] = !MASK || vi[v] < a.nvec;
+    }
+
+    float acc[V][8];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
+
+    // Rows that do not depend on the slot map are requested first, so their
+    // latency overlaps the gathers instead of following them.
+    u32x4 shv[V], resv[V], gmv[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        shv[v] = resv[v] = gmv[v] = (u32x4){0u, 0u, 0u, 0u};
+        if (!ok[v]) continue;
+        if constexpr (SH) shv[v] = ld_stream(a.shared + row_off + (int64_t)vi[v] * 8);
+        if constexpr (EPI == EPI_RMSNORM || EPI == EPI_RMSNORM_MXFP8) {
+            resv[v] = ld_stream(a.residual + row_off + (int64_t)vi[v] * 8);
+            if constexpr (V <= 4) gmv[v] = ld_cached(a.gamma + (int64_t)vi[v] * 8);
+        }
+    }
+
+    gather_sum<KT, V>(a, t, vi, ok, acc);
 
     if constexpr (SH) {
 #pragma unroll
