@@ -46,6 +46,12 @@ DESCR = {
 }
 
 
+
+def dispatch_tile():
+    """The dispatch scatter's workgroup shape as the library will pick it."""
+    t = os.environ.get("MOE_DISPATCH_TILE", "")
+    return t if t and t != "auto" else "64x2"
+
 def kernel_source_hash():
     """sha256 over the kernel and ABI sources; byte counters taken from an
     older kernel are not reported."""
@@ -295,7 +301,8 @@ def main():
                    "top_k": k, "ep_size": ep, "max_tokens_per_rank": mtpr,
                    "kept_slots": kept, "io_dtype": "bf16",
                    "seed": args.seed, "input_sets": nsets,
-                   "launch": ("4 kernels: histogram, scan, rank, token-order row scatter (64 x 2 vectors)"
+                   "launch": ("3 kernels: per-chunk count and stable rank, scan, token-order row "
+                              "scatter (" + dispatch_tile() + " threads x vectors)"
                               if kind == "dispatch" else
                               mc.describe_launch({"bf16": 0, "dense": 0, "rmsnorm": 1, "mxfp8": 2,
                                                   "rmsnorm_mxfp8": 3, "mxfp4": 4}[kind], T, H, k))},

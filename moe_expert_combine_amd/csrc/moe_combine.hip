@@ -6,6 +6,8 @@
 // allocates nothing, keeps no state between calls and never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -37,6 +39,7 @@ moe_status_t ok() {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 constexpr int kMaxTopK = 32;
+constexpr int64_t kPlaceMaxPairs = 1 << 16;   // one-kernel dispatch placement up to here (measured crossover)
 constexpr int kMaxThreads = 1024;
 constexpr int kMaxRmsHidden = 512 * 8 * 8;   // 512 threads x 8 vectors x 8 bf16
 
@@ -64,6 +67,45 @@ bool tile_override(int *threads, int *vec, int *kt) {
     *vec = v;
     *kt = n == 3 ? k : 0;
     return true;
+}
+
+// Scatter shape of the dispatch: "<threads>x<vectors>" from
+// MOE_DISPATCH_TILE for tuning sweeps, else one wave of two 16-byte vectors
+// per lane.
+void dispatch_tile(int *threads, int *vec) {
+    *threads = 64;
+    *vec = 2;
+    const char *s = getenv("MOE_DISPATCH_TILE");
+    if (!s || !*s || !strcmp(s, "auto")) return;
+    int t = 0, v = 0;
+    if (sscanf(s, "%dx%d", &t, &v) != 2) return;
+    if (t < 64 || t > kMaxThreads || t % 64 || !(v == 1 || v == 2 || v == 4 || v == 8)) return;
+    *threads = t;
+    *vec = v;
+}
+
+// Largest pair count (num_tokens * top_k) placed by the one-kernel path; its
+// redundant per-workgroup histograms grow with the pair count, the two-kernel
+// path pays one more launch. MOE_DISPATCH_PLACE_MAX_PAIRS overrides it for
+// tuning sweeps and tests (0 forces the two-kernel path).
+int64_t dispatch_place_max_pairs() {
+    const char *s = getenv("MOE_DISPATCH_PLACE_MAX_PAIRS");
+    if (s && *s) {
+        char *end = nullptr;
+        const long long v = strtoll(s, &end, 10);
+        if (end && *end == 0 && v >= 0) return v;
+    }
+    return kPlaceMaxPairs;
+}
+
+template <bool FROM_OFFS>
+void launch_scatter(int vec, dim3 grid, dim3 block, hipStream_t s, const moe::DispatchArgs &a) {
+    switch (vec) {
+        case 1: hipLaunchKernelGGL((moe::dispatch_scatter<1, FROM_OFFS>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((moe::dispatch_scatter<2, FROM_OFFS>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((moe::dispatch_scatter<4, FROM_OFFS>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((moe::dispatch_scatter<8, FROM_OFFS>), grid, block, 0, s, a); break;
+    }
 }
 
 moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
@@ -403,9 +445,9 @@ static int64_t dispatch_chunks(int64_t T, int32_t k) { return (T * k + moe::kChu
 size_t moe_dispatch_workspace_size(int64_t num_tokens, int32_t top_k, int32_t num_experts, int32_t ep_size,
                                    int64_t max_tokens_per_rank) {
     if (num_tokens < 0 || top_k < 1 || num_experts < 1 || ep_size < 1 || max_tokens_per_rank < 1) return 0;
-    // hist [nchunks, E] + base [E], int32 (ep_size and capacity are part of
-    // the signature so that the layout may depend on them)
-    const int64_t n = (dispatch_chunks(num_tokens, top_k) + 1) * (int64_t)num_experts * 4;
+    // offs [nchunks, E] + local [T * k], int32 (ep_size and capacity are
+    // part of the signature so that the layout may depend on them)
+    const int64_t n = (dispatch_chunks(num_tokens, top_k) * (int64_t)num_experts + num_tokens * top_k) * 4;
     return (size_t)((n + 255) / 256 * 256);
 }
 
@@ -444,21 +486,32 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_to
     a.recv_counts = recv_counts;
     a.pairs = num_tokens * top_k;
     a.nchunks = (int)dispatch_chunks(num_tokens, top_k);
-    a.hist = static_cast<int32_t *>(workspace);
-    a.base = a.hist + (int64_t)a.nchunks * num_experts;
+    a.offs = static_cast<int32_t *>(workspace);
+    a.local = a.offs + (int64_t)a.nchunks * num_experts;
     a.mtpr = max_tokens_per_rank;
     a.T = (int)num_tokens;
     a.H = hidden;
     a.k = top_k;
     a.E = num_experts;
     a.epr = num_experts / ep_size;
-    a.hchunks = (hidden / 8 + 127) / 128;
+    a.segs = std::max(1, std::min(a.nchunks, 1024 / a.epr));
+    a.idbits = 32 - __builtin_clz((unsigned)num_experts);
+    int sthreads = 0, svec = 0;
+    dispatch_tile(&sthreads, &svec);
+    a.hchunks = (hidden / 8 + sthreads * svec - 1) / (sthreads * svec);
     if ((int64_t)a.T * a.hchunks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(moe::dispatch_hist, dim3(a.nchunks), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(moe::dispatch_scan, dim3(1), dim3(1024), 0, s, a);
-    hipLaunchKernelGGL(moe::dispatch_rank, dim3(a.nchunks), dim3(64), 0, s, a);
-    hipLaunchKernelGGL(moe::dispatch_scatter<2>, dim3((unsigned)((int64_t)a.T * a.hchunks)), dim3(64), 0, s, a);
+    const bool small = a.pairs <= dispatch_place_max_pairs();
+    if (small) {
+        hipLaunchKernelGGL(moe::dispatch_place, dim3((unsigned)((a.pairs + moe::kPlaceChunk - 1) / moe::kPlaceChunk)),
+                           dim3(moe::kPlace), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(moe::dispatch_count, dim3(a.nchunks), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(moe::dispatch_scan, dim3(ep_size), dim3(1024), 0, s, a);
+    }
+    const dim3 sg((unsigned)((int64_t)a.T * a.hchunks)), sb(sthreads);
+    if (small) launch_scatter<false>(svec, sg, sb, s, a);
+    else launch_scatter<true>(svec, sg, sb, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

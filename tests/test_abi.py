@@ -147,7 +147,7 @@ def test_reduce_dense_argument_errors():
 
 def test_dispatch_argument_errors_and_workspace_size():
     L = mc.lib()
-    n = (4096 * 8 // 256 + 1) * 256 * 4
+    n = (4096 * 8 // 256 * 256 + 4096 * 8) * 4     # chunk offsets [chunks, E] + pair ranks [T * k]
     assert mc.dispatch_workspace_size(4096, 8, 256, 8, 4224) == (n + 255) // 256 * 256
     assert mc.dispatch_workspace_size(1, 1, 8, 1, 1) == 256     # rounded to 256 B
     assert mc.dispatch_workspace_size(-1, 8, 8, 1, 1) == 0

@@ -546,8 +546,14 @@ def _dispatch_case(T, H, k, E, ep, cap, drop, seed, bad_ids=False):
     (1500, 512, 4, 256, 4, None, 0.2, True),       # > one chunk, bad ids
     (2048, 2048, 8, 4096, 8, None, 0.0, False),    # maximum expert count
     (513, 96, 32, 32, 1, 200, 0.0, False),         # top_k = 32, tight capacity
+    (2000, 64, 8, 1024, 1, None, 0.0, False),      # 1024 experts on one rank: 63 chunks per column
+    (700, 64, 6, 4096, 2, None, 0.05, True),       # 2048 experts per rank
+    (4100, 64, 8, 4096, 1, 3000, 0.0, False),      # 4096 experts on one rank, capacity drops
 ])
-def test_dispatch_matches_oracle(T, H, k, E, ep, cap, drop, bad):
+@pytest.mark.parametrize("path", ["place", "count_scan"])
+def test_dispatch_matches_oracle(T, H, k, E, ep, cap, drop, bad, path, monkeypatch):
+    if path == "count_scan":                        # force the large-input path
+        monkeypatch.setenv("MOE_DISPATCH_PLACE_MAX_PAIRS", "0")
     x, ids, clean, cap = _dispatch_case(T, H, k, E, ep, cap, drop, seed=T + k, bad_ids=bad)
     poison = np.full((ep, cap, H), 0xFFFF, np.uint16)
     counts0 = np.arange(E, dtype=np.int32) % 7                 # accumulates onto this
@@ -582,8 +588,11 @@ def test_dispatch_identity_combine_round_trip_on_gpu():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["dsv3", "mxfp8"])
-def test_full_size_dispatch(name):
+@pytest.mark.parametrize("name,path", [("dsv3", "place"), ("dsv3", "count_scan"),
+                                       ("mxfp8", "place"), ("mxfp8", "count_scan")])
+def test_full_size_dispatch(name, path, monkeypatch):
+    if path == "count_scan":
+        monkeypatch.setenv("MOE_DISPATCH_PLACE_MAX_PAIRS", "0")
     inp = gen.make_inputs(dict(gen.CONFIGS[name], H=8), seed=0)   # routing only
     T, H, E = inp.T, gen.CONFIGS[name]["H"], inp.meta["E"]
     rng = np.random.default_rng(1)
@@ -602,11 +611,14 @@ def test_full_size_dispatch(name):
 
 # ------------------------------------------------------------ HIP graphs
 
-def test_hip_graph_capture_and_replay():
+@pytest.mark.parametrize("path", ["place", "count_scan"])
+def test_hip_graph_capture_and_replay(path, monkeypatch):
     """The entry points allocate nothing and never synchronise, so they can
-    be captured in a graph: dispatch (4 kernels) followed by the combine,
-    replayed three times with new input contents written eagerly between
-    replays; every replay matches the oracle."""
+    be captured in a graph: dispatch (either placement path) followed by the
+    combine, replayed three times with new input contents written eagerly
+    between replays; every replay matches the oracle."""
+    if path == "count_scan":
+        monkeypatch.setenv("MOE_DISPATCH_PLACE_MAX_PAIRS", "0")
     inp = gen.make_inputs(dict(T=200, H=1024, E=32, ep=4, k=4, drop_frac=0.1), seed=2)
     T, H, E = inp.T, inp.H, 32
     ids = inp.topk_ids.copy()
