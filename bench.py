@@ -52,9 +52,34 @@ def dispatch_tile():
     t = os.environ.get("MOE_DISPATCH_TILE", "")
     return t if t and t != "auto" else "64x2"
 
+def strip_comments(src):
+    """C/C++ source text without comments and with whitespace runs collapsed,
+    so that the hash below changes with the code, not with its comments."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":                                   # string or char literal
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
-    """sha256 over the kernel and ABI sources; byte counters taken from an
-    older kernel are not reported."""
+    """sha256 over the kernel and ABI sources, comments left out; byte
+    counters taken from other kernel code are not reported."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_expert_combine_amd", "csrc")
@@ -62,8 +87,8 @@ def kernel_source_hash():
     files.append(os.path.join(ROOT, "include", "moe_combine.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 
@@ -90,8 +115,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (the combine has no multi-GPU path here).", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the combine and dispatch have no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -1,0 +1,43 @@
+"""Host-side pieces of bench.py that need no GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_strip_comments_keeps_code_and_literals():
+    src = 'int a = 1; // note\n/* block\n comment */ const char *s = "x//y/*z*/";\nchar q = \'"\';  int b;'
+    assert bench.strip_comments(src) == 'int a = 1; const char *s = "x//y/*z*/"; char q = \'"\'; int b;'
+    assert bench.strip_comments('p = "a\\"//b"; // c') == 'p = "a\\"//b";'
+
+
+def test_source_hash_ignores_comments_not_code():
+    a = "__global__ void k(int *p) { p[0] = 1; }\n"
+    b = "// a comment\n__global__ void k(int *p) {\n    p[0] = 1;   /* same code */\n}\n"
+    c = "__global__ void k(int *p) { p[0] = 2; }\n"
+    assert bench.strip_comments(a) == bench.strip_comments(b)
+    assert bench.strip_comments(a) != bench.strip_comments(c)
+
+
+def test_traffic_files_name_their_workload():
+    for w in bench.DESCR:
+        p = os.path.join(ROOT, "profiles", f"traffic_{w}.json")
+        if not os.path.exists(p):
+            continue
+        d = json.load(open(p))
+        assert d["workload"] == w
+        assert d["bytes_per_launch"] == d["fetch_bytes"] + d["write_bytes"]
+        assert len(d["kernel_source_sha256"]) == 64
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
