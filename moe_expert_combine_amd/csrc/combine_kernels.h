@@ -279,7 +279,6 @@ __device__ __forceinline__ void gather_sum(const KernelArgs &a, int t, const int
                     acc[v][e] = __builtin_fmaf(w[jj], bf16_elem(x[jj][v], e), acc[v][e]);
         }
     }
-
 }
 
 // Register budget: KT * V 16-byte loads are in flight per lane (KT * V <= 16,
