@@ -549,6 +549,8 @@ def _dispatch_case(T, H, k, E, ep, cap, drop, seed, bad_ids=False):
     (2000, 64, 8, 1024, 1, None, 0.0, False),      # 1024 experts on one rank: 63 chunks per column
     (700, 64, 6, 4096, 2, None, 0.05, True),       # 2048 experts per rank
     (4100, 64, 8, 4096, 1, 3000, 0.0, False),      # 4096 experts on one rank, capacity drops
+    (64, 64, 4, 16, 4, 1, 0.0, False),             # capacity 1: one row per rank
+    (100, 64, 2, 8, 2, None, 1.0, False),          # every slot dropped: nothing placed
 ])
 @pytest.mark.parametrize("path", ["place", "count_scan"])
 def test_dispatch_matches_oracle(T, H, k, E, ep, cap, drop, bad, path, monkeypatch):
