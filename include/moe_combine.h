@@ -52,7 +52,8 @@
  *  - Outputs have at least num_tokens rows. Exactly the first num_tokens
  *    rows are written; rows past them are untouched. Outputs must not
  *    overlap any input, except where an entry point allows it.
- *  - hidden must be a positive multiple of 8 (16-byte rows). bf16 pointers
+ *  - hidden must be a positive multiple of 8 (16-byte rows), at most 2^28
+ *    (output rows are addressed with 32-bit byte offsets). bf16 pointers
  *    must be 16-byte aligned, src_info 8-byte aligned, router_weights 4-byte
  *    aligned. 1 <= top_k <= 32, ep_size >= 1, max_tokens_per_rank >= 1, and
  *    num_tokens >= 0. num_tokens == 0 returns MOE_OK and launches nothing.

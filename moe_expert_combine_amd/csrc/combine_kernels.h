@@ -80,23 +80,52 @@ __device__ __forceinline__ unsigned e4m3_mag(unsigned a) {
 }
 
 // Memory access helpers. Rows that are read once (payload, shared expert,
-// residual) use non-temporal loads and every output uses non-temporal stores:
-// on MI355X the streaming hint lifts a random-row gather from about 5.0 to
-// about 5.8 TB/s. gamma, reused by every token, takes ordinary loads.
+// residual) use non-temporal loads: on MI355X the streaming hint lifts a
+// random-row gather from about 5.0 to about 5.8 TB/s. gamma, reused by every
+// token, takes ordinary loads.
 __device__ __forceinline__ u32x4 ld_stream(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 __device__ __forceinline__ u32x4 ld_cached(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
+
+// Output stores, with the cache policy chosen per epilogue by measurement on
+// MI355X. The output stores are what a gather-sum pays most for beyond its
+// reads (the bf16 kernel without them runs in 71 us instead of 90 us at
+// T = 4096, H = 7168).
+//  - The bf16, MXFP8 and MXFP4 combines and the local reduce write through a
+//    buffer resource over the output row (its size as the range, so the
+//    hardware drops any store past it) with the SC1 cache policy:
+//    device-scope write-through, the L2 forwarding the lines at once instead
+//    of holding them dirty for a later eviction. That is 2-6% faster than
+//    non-temporal stores (bf16 at T = 4096, H = 7168: 87.7 against 90.5 us).
+//  - The RMSNorm epilogues, whose whole-token workgroups write their rows in
+//    one burst after the row reduction, keep non-temporal global stores for
+//    rows and codes and write-back byte stores for scales: SC1 there is 2-4%
+//    slower.
+constexpr int kPolSC1 = 16;   // CPol bits of the buffer stores
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_row(void *row, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(row, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_sc1(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolSC1);
+}
+__device__ __forceinline__ void st_sc1(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kPolSC1);
+}
+__device__ __forceinline__ void st_sc1(__amdgpu_buffer_rsrc_t r, int off, unsigned v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kPolSC1);
+}
+__device__ __forceinline__ void st_sc1_byte(__amdgpu_buffer_rsrc_t r, int off, unsigned char v) {
+    __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, kPolSC1);
+}
 __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 __device__ __forceinline__ void st_stream(uint8_t *p, u32x2 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
-}
-__device__ __forceinline__ void st_stream(uint8_t *p, unsigned v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<unsigned *>(p));
 }
 
 // fp32 magnitude bits -> float4 e2m1 code magnitude (0..7 for 0, 0.5, 1, 1.5,
@@ -142,11 +171,11 @@ __device__ __forceinline__ double block_sum(double v, double *lds) {
 // exponent field of amax minus 8, clamped at 0 (floor(log2 amax) - 8 + 127),
 // 0xFF for NaN/inf blocks, and codes are e4m3 of x * 2^-e. Must be reached by
 // every lane of the wave (no divergence around the DPP reads).
-template <int V>
+template <int V, bool SC1>
 __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const bool (&ok)[V],
-                                                  const int (&vi)[V], int64_t row_off,
-                                                  int64_t scale_row_off, uint8_t *codes,
-                                                  uint8_t *scales) {
+                                                  const int (&vi)[V], int H, uint8_t *codes_row,
+                                                  uint8_t *scales_row) {
+    const __amdgpu_buffer_rsrc_t rc = out_row(codes_row, H), rs = out_row(scales_row, H >> 5);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         int m = 0;
@@ -166,8 +195,13 @@ __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const 
             const unsigned code = sgn | e4m3_mag(__float_as_uint(q) & 0x7FFFFFFFu);
             o[e >> 2] |= code << ((e & 3) * 8);
         }
-        st_stream(codes + row_off + (int64_t)vi[v] * 8, o);
-        if ((threadIdx.x & 3) == 0) scales[scale_row_off + (vi[v] >> 2)] = (uint8_t)sbyte;
+        if constexpr (SC1) {
+            st_sc1(rc, vi[v] * 8, o);
+            if ((threadIdx.x & 3) == 0) st_sc1_byte(rs, vi[v] >> 2, (unsigned char)sbyte);
+        } else {
+            st_stream(codes_row + (int64_t)vi[v] * 8, o);
+            if ((threadIdx.x & 3) == 0) scales_row[vi[v] >> 2] = (uint8_t)sbyte;
+        }
     }
 }
 
@@ -179,9 +213,9 @@ __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const 
 // nibble of byte i, stored as one 4-byte word.
 template <int V>
 __device__ __forceinline__ void mx4_quantize_store(const float (&x)[V][8], const bool (&ok)[V],
-                                                   const int (&vi)[V], int64_t code_row_off,
-                                                   int64_t scale_row_off, uint8_t *codes,
-                                                   uint8_t *scales) {
+                                                   const int (&vi)[V], int H, uint8_t *codes_row,
+                                                   uint8_t *scales_row) {
+    const __amdgpu_buffer_rsrc_t rc = out_row(codes_row, H >> 1), rs = out_row(scales_row, H >> 5);
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         int m = 0;
@@ -199,8 +233,8 @@ __device__ __forceinline__ void mx4_quantize_store(const float (&x)[V][8], const
             const float q = x[v][e] * inv;
             o |= (sgn | e2m1_mag(__float_as_uint(q) & 0x7FFFFFFFu)) << (4 * e);
         }
-        st_stream(codes + code_row_off + (int64_t)vi[v] * 4, o);
-        if ((threadIdx.x & 3) == 0) scales[scale_row_off + (vi[v] >> 2)] = (uint8_t)sbyte;
+        st_sc1(rc, vi[v] * 4, o);
+        if ((threadIdx.x & 3) == 0) st_sc1_byte(rs, vi[v] >> 2, (unsigned char)sbyte);
     }
 }
 
@@ -340,14 +374,14 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
     }
 
     if constexpr (EPI == EPI_BF16) {
-        uint16_t *out = static_cast<uint16_t *>(a.out0);
+        const __amdgpu_buffer_rsrc_t ro = out_row(static_cast<uint16_t *>(a.out0) + row_off, a.H * 2);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             if (!ok[v]) continue;
             u32x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[v][2 * i], acc[v][2 * i + 1]);
-            st_stream(out + row_off + (int64_t)vi[v] * 8, o);
+            st_sc1(ro, vi[v] * 16, o);
         }
     } else if constexpr (EPI == EPI_RMSNORM || EPI == EPI_RMSNORM_MXFP8) {
         // flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters residual_in,
@@ -401,14 +435,14 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
             }
         }
         if constexpr (EPI == EPI_RMSNORM_MXFP8)
-            mx_quantize_store<V>(acc, ok, vi, row_off, (int64_t)t * (a.H >> 5),
-                                 static_cast<uint8_t *>(a.out1), static_cast<uint8_t *>(a.out2));
+            mx_quantize_store<V, false>(acc, ok, vi, a.H, static_cast<uint8_t *>(a.out1) + row_off,
+                                 static_cast<uint8_t *>(a.out2) + (int64_t)t * (a.H >> 5));
     } else if constexpr (EPI == EPI_MXFP8) {
-        mx_quantize_store<V>(acc, ok, vi, row_off, (int64_t)t * (a.H >> 5),
-                             static_cast<uint8_t *>(a.out0), static_cast<uint8_t *>(a.out1));
+        mx_quantize_store<V, true>(acc, ok, vi, a.H, static_cast<uint8_t *>(a.out0) + row_off,
+                             static_cast<uint8_t *>(a.out1) + (int64_t)t * (a.H >> 5));
     } else {
-        mx4_quantize_store<V>(acc, ok, vi, (int64_t)t * (a.H >> 1), (int64_t)t * (a.H >> 5),
-                              static_cast<uint8_t *>(a.out0), static_cast<uint8_t *>(a.out1));
+        mx4_quantize_store<V>(acc, ok, vi, a.H, static_cast<uint8_t *>(a.out0) + (int64_t)t * (a.H >> 1),
+                              static_cast<uint8_t *>(a.out1) + (int64_t)t * (a.H >> 5));
     }
 }
 

@@ -42,6 +42,7 @@ constexpr int kMaxTopK = 32;
 constexpr int64_t kPlaceMaxPairs = 1 << 16;   // one-kernel dispatch placement up to here (measured crossover)
 constexpr int kMaxThreads = 1024;
 constexpr int kMaxRmsHidden = 512 * 8 * 8;   // 512 threads x 8 vectors x 8 bf16
+constexpr int kMaxHidden = 1 << 28;           // output rows are addressed with 32-bit byte offsets
 
 // Launch shape of one call.
 struct Plan {
@@ -162,6 +163,7 @@ moe_status_t check_common(const void *payload, const int32_t *src_info, const fl
                           int64_t T, int32_t H, int32_t k, int32_t ep, int64_t mtpr) {
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %lld)", (long long)T);
     if (H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", H);
+    if (H > kMaxHidden) return fail(MOE_ERR_INVALID_ARG, "hidden must be <= %d (got %d)", kMaxHidden, H);
     if (k < 1 || k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, %d] (got %d)", kMaxTopK, k);
     if (ep < 1) return fail(MOE_ERR_INVALID_ARG, "ep_size must be >= 1 (got %d)", ep);
     if (mtpr < 1 || mtpr > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "max_tokens_per_rank must be in [1, 2^31) (got %lld)", (long long)mtpr);

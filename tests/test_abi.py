@@ -63,6 +63,7 @@ def call_combine(payload=A, src=A, w=A, shared=None, out=2 * A, T=4, H=64, k=2,
     (dict(T=-1), "num_tokens"),
     (dict(H=0), "hidden"),
     (dict(H=12), "hidden"),
+    (dict(H=(1 << 28) + 8), "hidden"),
     (dict(k=0), "top_k"),
     (dict(k=33), "top_k"),
     (dict(ep=0), "ep_size"),
