@@ -32,7 +32,8 @@ def test_traffic_files_name_their_workload():
             continue
         d = json.load(open(p))
         assert d["workload"] == w
-        assert d["bytes_per_launch"] == d["fetch_bytes"] + d["write_bytes"]
+        # each figure is rounded from the same scaled counter values
+        assert abs(d["bytes_per_launch"] - (d["fetch_bytes"] + d["write_bytes"])) <= 1
         assert len(d["kernel_source_sha256"]) == 64
 
 
