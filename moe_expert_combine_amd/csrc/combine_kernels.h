@@ -100,10 +100,11 @@ __device__ __forceinline__ u32x4 ld_cached(const uint16_t *p) {
 //    device-scope write-through, the L2 forwarding the lines at once instead
 //    of holding them dirty for a later eviction. That is 2-6% faster than
 //    non-temporal stores (bf16 at T = 4096, H = 7168: 87.7 against 90.5 us).
-//  - The RMSNorm epilogues, whose whole-token workgroups write their rows in
-//    one burst after the row reduction, keep non-temporal global stores for
-//    rows and codes and write-back byte stores for scales: SC1 there is 2-4%
-//    slower.
+//  - The RMSNorm epilogues write residual_out the same way, before the row
+//    reduction, but the rows and codes written after it with non-temporal
+//    global stores and the scales with write-back byte stores: at T = 2048,
+//    H = 7168 that mix takes 54.5 us (55.9 with MXFP8), against 55.9 us with
+//    every store non-temporal and 57.1 us with every store SC1.
 constexpr int kPolSC1 = 16;   // CPol bits of the buffer stores
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_row(void *row, int bytes) {
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
         //   n = residual_out * rstd * (gamma + weight_bias)
         // The statistic and the scaling are done in fp64 (each x^2 of a bf16
         // value is exact), so n matches a double-precision evaluation.
-        uint16_t *res_out = static_cast<uint16_t *>(a.out0);
+        const __amdgpu_buffer_rsrc_t rro = out_row(static_cast<uint16_t *>(a.out0) + row_off, a.H * 2);
         double ss = 0.0;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
                 acc[v][e] = xr;
                 ss = __builtin_fma((double)xr, (double)xr, ss);
             }
-            st_stream(res_out + row_off + (int64_t)vi[v] * 8, o);
+            st_sc1(rro, vi[v] * 16, o);
         }
         const double tot = block_sum(ss, lds_red);
         const double rstd = 1.0 / __builtin_sqrt(tot / (double)a.H + (double)a.eps);
