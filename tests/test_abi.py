@@ -238,6 +238,11 @@ def test_binding_rejects_host_tensors_and_bad_dtypes():
         mc.moe_combine(p, s)
     with pytest.raises(ValueError):
         mc.moe_combine_mxfp8(p.float(), s)
+    with pytest.raises(ValueError):
+        mc.moe_reduce_dense(torch.zeros((2, 4, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        mc.moe_dispatch(torch.zeros((4, 64), dtype=torch.bfloat16),
+                        torch.zeros((4, 2), dtype=torch.int32), 8, 2, 8)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
