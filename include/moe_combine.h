@@ -279,8 +279,8 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(
  * Launches: up to 65536 pairs (num_tokens * top_k), one placement kernel
  * and the row scatter; above, a count kernel, a scan kernel and the row
  * scatter (the workspace holds their intermediate counts). Tuning
- * overrides, read at each call: MOE_DISPATCH_PLACE_MAX_PAIRS=<n> moves the
- * switch point (0 always takes the three-kernel path), and
+ * overrides, read at each call: MOE_DISPATCH_PATH=place or count_scan
+ * takes that path at any size (both are exact at every size), and
  * MOE_DISPATCH_TILE="<threads>x<vectors>" sets the scatter's workgroup size
  * (a multiple of 64, at most 1024) and 16-byte vectors per thread (1, 2, 4
  * or 8). Invalid values are ignored.

@@ -195,25 +195,23 @@ __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs a) {
     }
 }
 
-// Small inputs: one kernel places every pair. Each workgroup of kPlace
-// threads histograms ALL ids in LDS, split at its first pair p0 (lo: pairs
-// before p0, hi: the rest), so it knows every expert's total and the row its
-// first pair of each expert takes without waiting for any other workgroup.
-// It then ranks its own kPlaceChunk pairs in order (wave w holds pairs
-// p0 + 64 w .. p0 + 64 w + 63; the waves take their turns at the running rows
-// in LDS between barriers) and writes their final (rank, row). The redundant
-// histograms cost O(pairs) per workgroup; the host takes this path only for
-// small pair counts, where it saves the launch of a second kernel (on MI355X
-// at 32768 pairs, 256 experts: 8.2 us against 11.4 us for count + scan).
-__global__ __launch_bounds__(kPlace) void dispatch_place(DispatchArgs a) {
-    __shared__ int lo[kMaxExperts];
-    __shared__ int hi[kMaxExperts];
-    __shared__ int wsum[kPlace / 64];
+// Placement of one chunk of pairs by a workgroup of kPlace threads, with no
+// other workgroup involved. It histograms ALL ids in LDS, split at the
+// chunk's first pair p0 (lo: pairs before p0, hi: the rest), so it knows
+// every expert's total and the row the chunk's first pair of each expert
+// takes. It then ranks the chunk's cnt <= kPlace pairs in order (wave w holds
+// pairs p0 + 64 w .. p0 + 64 w + 63; the waves take their turns at the
+// running rows in LDS between barriers), writes their src_info, and returns
+// thread i's pair p0 + i as (rank, row), (-1, -1) if dropped or past the
+// chunk. Workgroup 0 also adds the receive counts. Every thread of the
+// workgroup must call it. The redundant histograms cost O(pairs) per
+// workgroup, so the host uses it for small pair counts only.
+__device__ __forceinline__ int2 place_chunk(const DispatchArgs &a, int64_t p0, int cnt, int *lo, int *hi,
+                                            int *wsum) {
     const int E = a.E;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int64_t p0 = (int64_t)blockIdx.x * kPlaceChunk;
     const int64_t pm = p0 + tid;                        // this thread's own pair
-    const bool mine_ok = tid < kPlaceChunk && pm < a.pairs;
+    const bool mine_ok = tid < cnt && pm < a.pairs;
     const int myid = mine_ok ? clean_id(a.ids[pm], E) : -1;
     for (int e = tid; e < E; e += kPlace) lo[e] = hi[e] = 0;
     __syncthreads();
@@ -287,7 +285,7 @@ __global__ __launch_bounds__(kPlace) void dispatch_place(DispatchArgs a) {
     const uint64_t gt = (lane == 63) ? 0ull : (~0ull << (lane + 1));
     const int before = __popcll(same & lt);
     int row = -1;
-    for (int w = 0; w < kPlaceChunk / 64; ++w) {
+    for (int w = 0; w * 64 < cnt; ++w) {
         // one LDS read by all lanes, then the last lane of each id writes
         if (wid == w && myid >= 0) {
             row = lo[myid] + before;
@@ -295,11 +293,20 @@ __global__ __launch_bounds__(kPlace) void dispatch_place(DispatchArgs a) {
         }
         __syncthreads();
     }
-    if (mine_ok) {
-        int2 o = make_int2(-1, -1);
-        if (myid >= 0 && row < a.mtpr) o = make_int2(myid / a.epr, row);
-        reinterpret_cast<int2 *>(a.src_info)[pm] = o;
-    }
+    int2 o = make_int2(-1, -1);
+    if (myid >= 0 && row < a.mtpr) o = make_int2(myid / a.epr, row);
+    if (mine_ok) reinterpret_cast<int2 *>(a.src_info)[pm] = o;
+    return o;
+}
+
+// Small inputs, general hidden size: placement only, kPlaceChunk pairs per
+// workgroup (on MI355X at 32768 pairs, 256 experts: 8.2 us against 11.4 us
+// for count + scan); the scatter follows.
+__global__ __launch_bounds__(kPlace) void dispatch_place(DispatchArgs a) {
+    __shared__ int lo[kMaxExperts];
+    __shared__ int hi[kMaxExperts];
+    __shared__ int wsum[kPlace / 64];
+    place_chunk(a, (int64_t)blockIdx.x * kPlaceChunk, kPlaceChunk, lo, hi, wsum);
 }
 
 typedef unsigned int du32x4 __attribute__((ext_vector_type(4)));

@@ -85,18 +85,19 @@ void dispatch_tile(int *threads, int *vec) {
     *vec = v;
 }
 
-// Largest pair count (num_tokens * top_k) placed by the one-kernel path; its
-// redundant per-workgroup histograms grow with the pair count, the two-kernel
-// path pays one more launch. MOE_DISPATCH_PLACE_MAX_PAIRS overrides it for
-// tuning sweeps and tests (0 forces the two-kernel path).
-int64_t dispatch_place_max_pairs() {
-    const char *s = getenv("MOE_DISPATCH_PLACE_MAX_PAIRS");
-    if (s && *s) {
-        char *end = nullptr;
-        const long long v = strtoll(s, &end, 10);
-        if (end && *end == 0 && v >= 0) return v;
-    }
-    return kPlaceMaxPairs;
+// Dispatch paths. Placement by redundant per-workgroup histograms (place)
+// grows with the pair count; the count + scan path pays one more launch. Up
+// to kPlaceMaxPairs pairs: place + scatter; above: count + scan + scatter.
+// MOE_DISPATCH_PATH = place | count_scan forces a path for tuning sweeps and
+// tests (both are correct at every size).
+enum DispatchPath { PATH_COUNT_SCAN = 0, PATH_PLACE = 1 };
+
+DispatchPath dispatch_path(int64_t pairs) {
+    DispatchPath p = pairs <= kPlaceMaxPairs ? PATH_PLACE : PATH_COUNT_SCAN;
+    const char *s = getenv("MOE_DISPATCH_PATH");
+    if (s && !strcmp(s, "count_scan")) p = PATH_COUNT_SCAN;
+    if (s && !strcmp(s, "place")) p = PATH_PLACE;
+    return p;
 }
 
 template <bool FROM_OFFS>
@@ -503,17 +504,16 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_to
     a.hchunks = (hidden / 8 + sthreads * svec - 1) / (sthreads * svec);
     if ((int64_t)a.T * a.hchunks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool small = a.pairs <= dispatch_place_max_pairs();
-    if (small) {
+    const dim3 sg((unsigned)((int64_t)a.T * a.hchunks)), sb(sthreads);
+    if (dispatch_path(a.pairs) == PATH_PLACE) {
         hipLaunchKernelGGL(moe::dispatch_place, dim3((unsigned)((a.pairs + moe::kPlaceChunk - 1) / moe::kPlaceChunk)),
                            dim3(moe::kPlace), 0, s, a);
+        launch_scatter<false>(svec, sg, sb, s, a);
     } else {
         hipLaunchKernelGGL(moe::dispatch_count, dim3(a.nchunks), dim3(64), 0, s, a);
         hipLaunchKernelGGL(moe::dispatch_scan, dim3(ep_size), dim3(1024), 0, s, a);
+        launch_scatter<true>(svec, sg, sb, s, a);
     }
-    const dim3 sg((unsigned)((int64_t)a.T * a.hchunks)), sb(sthreads);
-    if (small) launch_scatter<false>(svec, sg, sb, s, a);
-    else launch_scatter<true>(svec, sg, sb, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -554,8 +554,7 @@ def _dispatch_case(T, H, k, E, ep, cap, drop, seed, bad_ids=False):
 ])
 @pytest.mark.parametrize("path", ["place", "count_scan"])
 def test_dispatch_matches_oracle(T, H, k, E, ep, cap, drop, bad, path, monkeypatch):
-    if path == "count_scan":                        # force the large-input path
-        monkeypatch.setenv("MOE_DISPATCH_PLACE_MAX_PAIRS", "0")
+    monkeypatch.setenv("MOE_DISPATCH_PATH", path)
     x, ids, clean, cap = _dispatch_case(T, H, k, E, ep, cap, drop, seed=T + k, bad_ids=bad)
     poison = np.full((ep, cap, H), 0xFFFF, np.uint16)
     counts0 = np.arange(E, dtype=np.int32) % 7                 # accumulates onto this
@@ -593,8 +592,7 @@ def test_dispatch_identity_combine_round_trip_on_gpu():
 @pytest.mark.parametrize("name,path", [("dsv3", "place"), ("dsv3", "count_scan"),
                                        ("mxfp8", "place"), ("mxfp8", "count_scan")])
 def test_full_size_dispatch(name, path, monkeypatch):
-    if path == "count_scan":
-        monkeypatch.setenv("MOE_DISPATCH_PLACE_MAX_PAIRS", "0")
+    monkeypatch.setenv("MOE_DISPATCH_PATH", path)
     inp = gen.make_inputs(dict(gen.CONFIGS[name], H=8), seed=0)   # routing only
     T, H, E = inp.T, gen.CONFIGS[name]["H"], inp.meta["E"]
     rng = np.random.default_rng(1)
@@ -619,8 +617,7 @@ def test_hip_graph_capture_and_replay(path, monkeypatch):
     be captured in a graph: dispatch (either placement path) followed by the
     combine, replayed three times with new input contents written eagerly
     between replays; every replay matches the oracle."""
-    if path == "count_scan":
-        monkeypatch.setenv("MOE_DISPATCH_PLACE_MAX_PAIRS", "0")
+    monkeypatch.setenv("MOE_DISPATCH_PATH", path)
     inp = gen.make_inputs(dict(T=200, H=1024, E=32, ep=4, k=4, drop_frac=0.1), seed=2)
     T, H, E = inp.T, inp.H, 32
     ids = inp.topk_ids.copy()
