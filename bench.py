@@ -47,11 +47,6 @@ DESCR = {
 
 
 
-def dispatch_tile():
-    """The dispatch scatter's workgroup shape as the library will pick it."""
-    t = os.environ.get("MOE_DISPATCH_TILE", "")
-    return t if t and t != "auto" else "64x2"
-
 def strip_comments(src):
     """C/C++ source text without comments and with whitespace runs collapsed,
     so that the hash below changes with the code, not with its comments."""
@@ -326,11 +321,9 @@ def main():
                    "top_k": k, "ep_size": ep, "max_tokens_per_rank": mtpr,
                    "kept_slots": kept, "io_dtype": "bf16",
                    "seed": args.seed, "input_sets": nsets,
-                   "launch": ("3 kernels: per-chunk count and stable rank, scan, token-order row "
-                              "scatter (" + dispatch_tile() + " threads x vectors)"
-                              if kind == "dispatch" else
-                              mc.describe_launch({"bf16": 0, "dense": 0, "rmsnorm": 1, "mxfp8": 2,
-                                                  "rmsnorm_mxfp8": 3, "mxfp4": 4}[kind], T, H, k))},
+                   "launch": mc.describe_launch({"bf16": 0, "dense": 0, "rmsnorm": 1, "mxfp8": 2,
+                                                 "rmsnorm_mxfp8": 3, "mxfp4": 4,
+                                                 "dispatch": 5}[kind], T, H, k)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": algo_bytes,

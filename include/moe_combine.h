@@ -306,11 +306,13 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids,
 /*
  * Describes the launch an entry point would make for these sizes, without
  * touching the GPU. kind: 0 = moe_combine, 1 = residual + RMSNorm,
- * 2 = MXFP8, 3 = residual + RMSNorm + MXFP8, 4 = MXFP4.
+ * 2 = MXFP8, 3 = residual + RMSNorm + MXFP8, 4 = MXFP4, 5 = moe_dispatch.
  *
  * On success, writes a NUL-terminated text into buf, such as
- * "threads=128 vec_per_thread=1 chunks=7 blocks=28672 slot_tile=8 masked=0",
- * and returns MOE_OK. It validates the sizes like the entry point does.
+ * "threads=128 vec_per_thread=1 chunks=7 blocks=28672 slot_tile=8 masked=0"
+ * (or, for the dispatch, "path=place place_blocks=128 scatter_threads=64
+ * scatter_vec_per_thread=2 scatter_blocks=28672"), and returns MOE_OK. It
+ * validates the sizes like the entry point does.
  * The environment variable MOE_COMBINE_TILE="<threads>x<vectors>[x<kt>]"
  * overrides the threads per block and the 16-byte vectors per thread of
  * every combine entry point. kt, one of 2, 4 or 8, caps the slot tile, the

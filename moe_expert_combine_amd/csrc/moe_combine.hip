@@ -521,8 +521,24 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_to
 
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,
                                          int32_t buflen) {
-    if (kind < 0 || kind > 4) return fail(MOE_ERR_INVALID_ARG, "kind must be in [0, 4]");
+    if (kind < 0 || kind > 5) return fail(MOE_ERR_INVALID_ARG, "kind must be in [0, 5]");
     if (!buf || buflen < 1) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or empty");
+    if (kind == 5) {
+        if (num_tokens < 0 || num_tokens > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be in [0, 2^31)");
+        if (hidden <= 0 || hidden % 8) return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", hidden);
+        if (top_k < 1 || top_k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, %d] (got %d)", kMaxTopK, top_k);
+        if (num_tokens * (int64_t)top_k > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens * top_k must be < 2^31");
+        int sthreads = 0, svec = 0;
+        dispatch_tile(&sthreads, &svec);
+        const int64_t pairs = num_tokens * top_k;
+        const int64_t hchunks = (hidden / 8 + sthreads * svec - 1) / (sthreads * svec);
+        const bool place = dispatch_path(pairs) == PATH_PLACE;
+        snprintf(buf, (size_t)buflen, "path=%s place_blocks=%lld scatter_threads=%d scatter_vec_per_thread=%d "
+                 "scatter_blocks=%lld", place ? "place" : "count_scan",
+                 place ? (long long)((pairs + moe::kPlaceChunk - 1) / moe::kPlaceChunk) : 0LL, sthreads, svec,
+                 (long long)(num_tokens * hchunks));
+        return ok();
+    }
     moe_status_t st = check_common(reinterpret_cast<const void *>(16), reinterpret_cast<const int32_t *>(16), nullptr,
                                    nullptr, num_tokens, hidden, top_k, 1, 1);
     if (st != MOE_OK) return st;

@@ -272,3 +272,24 @@ def test_product_and_oracle_share_no_code():
     for f in _py_sources("gen"):
         txt = open(f).read()
         assert "import oracle" not in txt and "moe_expert_combine_amd" not in txt, f
+
+
+def test_describe_dispatch_launch(monkeypatch):
+    monkeypatch.delenv("MOE_DISPATCH_PATH", raising=False)
+    monkeypatch.delenv("MOE_DISPATCH_TILE", raising=False)
+    d = mc.describe_launch(5, 4096, 7168, 8)
+    assert d == ("path=place place_blocks=128 scatter_threads=64 scatter_vec_per_thread=2 "
+                 "scatter_blocks=28672")
+    assert mc.describe_launch(5, 8192, 7168, 8).startswith("path=place ")      # 65536 pairs
+    assert mc.describe_launch(5, 8193, 7168, 8).startswith("path=count_scan ")
+    monkeypatch.setenv("MOE_DISPATCH_PATH", "count_scan")
+    assert mc.describe_launch(5, 16, 64, 2).startswith("path=count_scan ")
+    monkeypatch.setenv("MOE_DISPATCH_PATH", "place")
+    assert mc.describe_launch(5, 16384, 7168, 8).startswith("path=place place_blocks=512 ")
+    monkeypatch.setenv("MOE_DISPATCH_TILE", "448x2")
+    assert "scatter_threads=448 scatter_vec_per_thread=2 scatter_blocks=16384" in \
+        mc.describe_launch(5, 16384, 7168, 8)
+    with pytest.raises(mc.MoeCombineError):
+        mc.describe_launch(6, 16, 64, 2)
+    with pytest.raises(mc.MoeCombineError):
+        mc.describe_launch(5, 16, 12, 2)
