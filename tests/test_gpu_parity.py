@@ -316,6 +316,29 @@ def test_ragged_and_edge_shapes(T, H, k, ep, extra):
     check_all_kinds(gen.make_inputs(c, seed=T), what=f"T={T} H={H} k={k}")
 
 
+def _random_combine_case(i):
+    """Seeded random shape: top_k, ranks, experts, hidden (multiples of 8,
+    ragged or not), drops, routing law, shared expert and unit weights."""
+    rng = np.random.default_rng(7000 + i)
+    k = int(rng.choice([1, 2, 3, 4, 6, 8, 13, 16, 32]))
+    ep = int(rng.choice([1, 2, 3, 4, 8]))
+    E = ep * max(-(-k // ep), int(rng.integers(1, 9)))
+    c = dict(T=int(rng.integers(1, 80)), k=k, ep=ep, E=E,
+             H=int(rng.choice([8, 32, 96, 264, 520, 1000, 1024, 2056, 4096, 7168])),
+             drop_frac=float(rng.choice([0.0, 0.0, 0.1, 0.5])),
+             weights=bool(rng.random() < 0.8),
+             routing="zipf" if rng.random() < 0.3 else "uniform")
+    if rng.random() < 0.4:
+        c["shared_sd"] = 0.5
+    return with_norm_inputs(c)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes_every_output(i):
+    c = _random_combine_case(i)
+    check_all_kinds(gen.make_inputs(c, seed=i), what=f"random case {i}: {c}")
+
+
 def test_unoccupied_nan_rows_and_all_dropped_tokens():
     c = with_norm_inputs(dict(T=48, H=1024, E=32, ep=4, k=8, unoccupied="nan",
                               drop_frac=0.4, shared_sd=0.5))
@@ -567,6 +590,30 @@ def test_dispatch_matches_oracle(T, H, k, E, ep, cap, drop, bad, path, monkeypat
     np.testing.assert_array_equal(src.cpu().numpy(), rs)
     np.testing.assert_array_equal(host16(pay), rp)               # placed rows and untouched ones
     np.testing.assert_array_equal(cnt.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("path", ["place", "count_scan"])
+def test_dispatch_random_shapes(i, path, monkeypatch):
+    monkeypatch.setenv("MOE_DISPATCH_PATH", path)
+    rng = np.random.default_rng(9000 + i)
+    k = int(rng.choice([1, 2, 4, 8, 32]))
+    ep = int(rng.choice([1, 2, 4, 8]))
+    E = ep * max(-(-k // ep), int(rng.choice([1, 3, 16, 64, 512])))
+    T = int(rng.integers(1, 3000))
+    H = int(rng.choice([8, 64, 264, 1024]))
+    cap = None if rng.random() < 0.5 else int(rng.integers(1, max(2, T * k // ep)))
+    drop = float(rng.choice([0.0, 0.2]))
+    x, ids, clean, cap = _dispatch_case(T, H, k, E, ep, cap, drop, seed=i, bad_ids=bool(rng.random() < 0.3))
+    counts0 = np.zeros(E, dtype=np.int32)
+    rp, rs, rc = oracle.dispatch(x, clean, E, ep, cap, recv_counts=counts0.copy())
+    cnt = torch.from_numpy(counts0).to(DEV)
+    pay, src = mc.moe_dispatch(dev16(x), torch.from_numpy(ids).to(DEV), E, ep, cap, recv_counts=cnt)
+    torch.cuda.synchronize()
+    what = f"T={T} H={H} k={k} E={E} ep={ep} cap={cap}"
+    np.testing.assert_array_equal(src.cpu().numpy(), rs, err_msg=what)
+    np.testing.assert_array_equal(host16(pay), rp, err_msg=what)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rc, err_msg=what)
 
 
 def test_dispatch_identity_combine_round_trip_on_gpu():
