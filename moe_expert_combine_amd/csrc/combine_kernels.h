@@ -175,8 +175,10 @@ __device__ __forceinline__ double block_sum(double v, double *lds) {
 template <int V, bool SC1>
 __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const bool (&ok)[V],
                                                   const int (&vi)[V], int H, uint8_t *codes_row,
-                                                  uint8_t *scales_row) {
+                                                  uint8_t *scales_row, bool full = false) {
     const __amdgpu_buffer_rsrc_t rc = out_row(codes_row, H), rs = out_row(scales_row, H >> 5);
+    u32x2 ov[V];
+    unsigned sb[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         int m = 0;
@@ -196,12 +198,43 @@ __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const 
             const unsigned code = sgn | e4m3_mag(__float_as_uint(q) & 0x7FFFFFFFu);
             o[e >> 2] |= code << ((e & 3) * 8);
         }
+        ov[v] = o;
+        sb[v] = sbyte;
+        if constexpr (SC1 && V == 2) {
+            if (full) continue;                    // merged store below
+        }
         if constexpr (SC1) {
             st_sc1(rc, vi[v] * 8, o);
             if ((threadIdx.x & 3) == 0) st_sc1_byte(rs, vi[v] >> 2, (unsigned char)sbyte);
         } else {
             st_stream(codes_row + (int64_t)vi[v] * 8, o);
             if ((threadIdx.x & 3) == 0) scales_row[vi[v] >> 2] = (uint8_t)sbyte;
+        }
+    }
+    if constexpr (SC1 && V == 2) {
+        if (full) {
+            // lane l stores the codes of vectors 2j, 2j + 1 (j = l % 32) of
+            // half l / 32, gathered from lanes 2j and 2j + 1: one 16-byte
+            // store per lane instead of two 8-byte ones
+            const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+            const int s0 = 2 * j, s1 = 2 * j + 1;
+            const unsigned a0 = __shfl(ov[0][0], s0), a1 = __shfl(ov[0][1], s0);
+            const unsigned b0 = __shfl(ov[0][0], s1), b1 = __shfl(ov[0][1], s1);
+            const unsigned c0 = __shfl(ov[1][0], s0), c1 = __shfl(ov[1][1], s0);
+            const unsigned d0 = __shfl(ov[1][0], s1), d1 = __shfl(ov[1][1], s1);
+            const u32x4 w = h ? (u32x4){c0, c1, d0, d1} : (u32x4){a0, a1, b0, b1};
+            const int base = vi[h] - lane + 2 * j;     // vector of this piece's first half
+            st_sc1(rc, base * 8, w);
+            // scale bytes: lane l < 8 stores bytes 4l..4l+3 of the wave's 16 + 16
+            const int qh = lane >> 2 & 1;               // which half (v) for lanes 0..7
+            const int qs = (lane & 3) * 16;            // first source lane of 4 quads
+            const unsigned s_0 = __shfl((int)sb[0], qs), s_1 = __shfl((int)sb[0], qs + 4);
+            const unsigned s_2 = __shfl((int)sb[0], qs + 8), s_3 = __shfl((int)sb[0], qs + 12);
+            const unsigned t_0 = __shfl((int)sb[1], qs), t_1 = __shfl((int)sb[1], qs + 4);
+            const unsigned t_2 = __shfl((int)sb[1], qs + 8), t_3 = __shfl((int)sb[1], qs + 12);
+            const unsigned word = qh ? (t_0 | t_1 << 8 | t_2 << 16 | t_3 << 24)
+                                     : (s_0 | s_1 << 8 | s_2 << 16 | s_3 << 24);
+            if (lane < 8) st_sc1(rs, ((vi[qh] - lane) >> 2) + (lane & 3) * 4, word);
         }
     }
 }
@@ -440,7 +473,8 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
                                  static_cast<uint8_t *>(a.out2) + (int64_t)t * (a.H >> 5));
     } else if constexpr (EPI == EPI_MXFP8) {
         mx_quantize_store<V, true>(acc, ok, vi, a.H, static_cast<uint8_t *>(a.out0) + row_off,
-                             static_cast<uint8_t *>(a.out1) + (int64_t)t * (a.H >> 5));
+                             static_cast<uint8_t *>(a.out1) + (int64_t)t * (a.H >> 5),
+                             (c + 1) * V * nt <= a.nvec && (a.H & 127) == 0);
     } else {
         mx4_quantize_store<V>(acc, ok, vi, a.H, static_cast<uint8_t *>(a.out0) + (int64_t)t * (a.H >> 1),
                               static_cast<uint8_t *>(a.out1) + (int64_t)t * (a.H >> 5));
