@@ -164,6 +164,25 @@ __device__ __forceinline__ double block_sum(double v, double *lds) {
     return s;
 }
 
+// The UE8M0 scale bytes of one wave holding two vectors per lane, all in
+// range: 16 bytes for each vector index v (one per DPP quad), stored as
+// eight 4-byte words (lanes 0..3: v = 0, lanes 4..7: v = 1) instead of 32
+// byte stores. vi0, vi1: this lane's two vector indices.
+__device__ __forceinline__ void st_scales_wave(__amdgpu_buffer_rsrc_t rs, unsigned sb0, unsigned sb1, int vi0,
+                                               int vi1) {
+    const int lane = threadIdx.x & 63;
+    const int qs = (lane & 3) * 16;                     // first of the word's 4 quads
+    unsigned w0 = 0u, w1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w0 |= (unsigned)__shfl((int)sb0, qs + 4 * i) << (8 * i);
+        w1 |= (unsigned)__shfl((int)sb1, qs + 4 * i) << (8 * i);
+    }
+    const bool second = lane & 4;
+    const int first_vec = (second ? vi1 : vi0) - lane;   // the wave's first vector of that half
+    if (lane < 8) st_sc1(rs, (first_vec >> 2) + (lane & 3) * 4, second ? w1 : w0);
+}
+
 // MXFP8 quantisation of V vectors of 8 fp32 values held by this lane
 // (flashinfer.comm.moe_a2a_combine, Parameters output_dtype float8_e4m3fn and
 // output_scales UE8M0 with 32 elements per scale). A 32-element block is the
@@ -223,18 +242,8 @@ __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const 
             const unsigned c0 = __shfl(ov[1][0], s0), c1 = __shfl(ov[1][1], s0);
             const unsigned d0 = __shfl(ov[1][0], s1), d1 = __shfl(ov[1][1], s1);
             const u32x4 w = h ? (u32x4){c0, c1, d0, d1} : (u32x4){a0, a1, b0, b1};
-            const int base = vi[h] - lane + 2 * j;     // vector of this piece's first half
-            st_sc1(rc, base * 8, w);
-            // scale bytes: lane l < 8 stores bytes 4l..4l+3 of the wave's 16 + 16
-            const int qh = lane >> 2 & 1;               // which half (v) for lanes 0..7
-            const int qs = (lane & 3) * 16;            // first source lane of 4 quads
-            const unsigned s_0 = __shfl((int)sb[0], qs), s_1 = __shfl((int)sb[0], qs + 4);
-            const unsigned s_2 = __shfl((int)sb[0], qs + 8), s_3 = __shfl((int)sb[0], qs + 12);
-            const unsigned t_0 = __shfl((int)sb[1], qs), t_1 = __shfl((int)sb[1], qs + 4);
-            const unsigned t_2 = __shfl((int)sb[1], qs + 8), t_3 = __shfl((int)sb[1], qs + 12);
-            const unsigned word = qh ? (t_0 | t_1 << 8 | t_2 << 16 | t_3 << 24)
-                                     : (s_0 | s_1 << 8 | s_2 << 16 | s_3 << 24);
-            if (lane < 8) st_sc1(rs, ((vi[qh] - lane) >> 2) + (lane & 3) * 4, word);
+            st_sc1(rc, (vi[h] - lane + 2 * j) * 8, w);
+            st_scales_wave(rs, sb[0], sb[1], vi[0], vi[1]);
         }
     }
 }
@@ -248,8 +257,9 @@ __device__ __forceinline__ void mx_quantize_store(const float (&x)[V][8], const 
 template <int V>
 __device__ __forceinline__ void mx4_quantize_store(const float (&x)[V][8], const bool (&ok)[V],
                                                    const int (&vi)[V], int H, uint8_t *codes_row,
-                                                   uint8_t *scales_row) {
+                                                   uint8_t *scales_row, bool full = false) {
     const __amdgpu_buffer_rsrc_t rc = out_row(codes_row, H >> 1), rs = out_row(scales_row, H >> 5);
+    unsigned ov[V], sb[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
         int m = 0;
@@ -267,8 +277,25 @@ __device__ __forceinline__ void mx4_quantize_store(const float (&x)[V][8], const
             const float q = x[v][e] * inv;
             o |= (sgn | e2m1_mag(__float_as_uint(q) & 0x7FFFFFFFu)) << (4 * e);
         }
+        ov[v] = o;
+        sb[v] = sbyte;
+        if constexpr (V == 2) {
+            if (full) continue;                    // merged store below
+        }
         st_sc1(rc, vi[v] * 4, o);
         if ((threadIdx.x & 3) == 0) st_sc1_byte(rs, vi[v] >> 2, (unsigned char)sbyte);
+    }
+    if constexpr (V == 2) {
+        if (full) {
+            // as for MXFP8: lane l stores the codes of vectors 2j, 2j + 1
+            // (j = l % 32) of half l / 32 as one 8-byte word
+            const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+            const unsigned a0 = __shfl(ov[0], 2 * j), a1 = __shfl(ov[0], 2 * j + 1);
+            const unsigned b0 = __shfl(ov[1], 2 * j), b1 = __shfl(ov[1], 2 * j + 1);
+            const u32x2 w = h ? (u32x2){b0, b1} : (u32x2){a0, a1};
+            st_sc1(rc, (vi[h] - lane + 2 * j) * 4, w);
+            st_scales_wave(rs, sb[0], sb[1], vi[0], vi[1]);
+        }
     }
 }
 
@@ -477,7 +504,8 @@ __global__ __launch_bounds__(max_threads_for<V>()) void combine_kernel(KernelArg
                              (c + 1) * V * nt <= a.nvec && (a.H & 127) == 0);
     } else {
         mx4_quantize_store<V>(acc, ok, vi, a.H, static_cast<uint8_t *>(a.out0) + (int64_t)t * (a.H >> 1),
-                              static_cast<uint8_t *>(a.out1) + (int64_t)t * (a.H >> 5));
+                              static_cast<uint8_t *>(a.out1) + (int64_t)t * (a.H >> 5),
+                              (c + 1) * V * nt <= a.nvec && (a.H & 127) == 0);
     }
 }
 
