@@ -339,6 +339,39 @@ def test_random_shapes_every_output(i):
     check_all_kinds(gen.make_inputs(c, seed=i), what=f"random case {i}: {c}")
 
 
+def test_mx_outputs_at_minimum_alignment():
+    """Code and scale arrays only as aligned as the entry points require
+    (e4m3 8 bytes, e2m1 4 bytes, scales 1 byte): the wider paired stores
+    must not be taken, and every byte must still match the oracle."""
+    inp = gen.make_inputs(with_norm_inputs(dict(T=40, H=2048, E=64, ep=8, k=8, shared_sd=0.5)), 3)
+    d = to_dev(inp)
+    T, H = inp.T, inp.H
+    big = torch.full((T * H + 64,), POISON8, dtype=torch.uint8, device=DEV)
+    sbig = torch.full((T * (H // 32) + 64,), POISON8, dtype=torch.uint8, device=DEV)
+    codes = big[8:8 + T * H].view(T, H)                       # 8-byte aligned only
+    scales = sbig[1:1 + T * (H // 32)].view(T, H // 32)       # 1-byte aligned
+    mc.moe_combine_mxfp8(d["payload"], d["src_info"], d["weights"], d["shared"],
+                         out_fp8=codes.view(torch.float8_e4m3fn), out_scales=scales)
+    rc, rs = oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights, inp.shared)
+    check_mxfp8(codes.cpu().numpy(), scales.cpu().numpy(), rc, rs, "mxfp8 at minimum alignment")
+    assert (big[:8].cpu().numpy() == POISON8).all() and (sbig[:1].cpu().numpy() == POISON8).all()
+
+    ro = poisoned16(T, H)
+    c2 = big[8:8 + T * H].view(T, H)
+    mc.moe_combine_residual_rmsnorm_mxfp8(d["payload"], d["src_info"], d["weights"], d["shared"],
+                                          d["residual"], d["gamma"], inp.eps, 1.0, residual_out=ro,
+                                          out_fp8=c2.view(torch.float8_e4m3fn), out_scales=scales)
+    rro, rno, rc2, rs2 = oracle.combine_residual_rmsnorm_mxfp8(
+        inp.payload, inp.src_info, inp.weights, inp.shared, inp.residual, inp.gamma, inp.eps, 1.0)
+    check_mxfp8(c2.cpu().numpy(), scales.cpu().numpy(), rc2, rs2, "rmsnorm+mxfp8 at minimum alignment")
+
+    c4 = big[4:4 + T * (H // 2)].view(T, H // 2)              # 4-byte aligned only
+    mc.moe_combine_mxfp4(d["payload"], d["src_info"], d["weights"], d["shared"],
+                         out_fp4=c4, out_scales=scales)
+    rc4, rs4 = oracle.combine_mxfp4(inp.payload, inp.src_info, inp.weights, inp.shared)
+    check_mxfp4(c4.cpu().numpy(), scales.cpu().numpy(), rc4, rs4, "mxfp4 at minimum alignment")
+
+
 def test_unoccupied_nan_rows_and_all_dropped_tokens():
     c = with_norm_inputs(dict(T=48, H=1024, E=32, ep=4, k=8, unoccupied="nan",
                               drop_frac=0.4, shared_sd=0.5))
