@@ -446,6 +446,23 @@ def test_e4m3_conversion_every_bf16_pattern():
     np.testing.assert_array_equal(codes, rc)
 
 
+def test_mxfp8_codes_identical_on_fp32_sums():
+    """Weighted sums of eight rows have full 24-bit mantissas, so they hit
+    e4m3 rounding boundaries the bf16 patterns above cannot; the codes of
+    both MXFP8 epilogues must still equal the oracle's exactly."""
+    inp = gen.make_inputs(with_norm_inputs(dict(T=512, H=7168, E=256, ep=8, k=8, shared_sd=0.5,
+                                                hot_row_frac=0.01, hot_scale=64.0)), 5)
+    c, s = run_mxfp8(inp)
+    rc, rs = oracle_all(inp, "mxfp8")
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+    _, _, c2, s2 = run_rmsnorm_mxfp8(inp, 1.0, want_norm=False)
+    _, _, rc2, rs2 = oracle.combine_residual_rmsnorm_mxfp8(
+        inp.payload, inp.src_info, inp.weights, inp.shared, inp.residual, inp.gamma, inp.eps, 1.0)
+    np.testing.assert_array_equal(s2, rs2)
+    np.testing.assert_array_equal(c2, rc2)
+
+
 def test_e2m1_conversion_every_bf16_pattern():
     """All 65536 bf16 patterns as single-slot sums through the MXFP4 path."""
     H = 1024
