@@ -321,8 +321,16 @@ typedef unsigned int du32x4 __attribute__((ext_vector_type(4)));
 // than non-temporal stores, unlike the combine's sequential output rows.
 template <int V, bool FROM_OFFS>
 __global__ __launch_bounds__(1024) void dispatch_scatter(DispatchArgs a) {
-    const int t = blockIdx.x / a.hchunks;
-    const int c = blockIdx.x - t * a.hchunks;
+    // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that
+    // each XCD takes one contiguous range of (token, chunk) pairs. All chunks
+    // of a token then run on one XCD, so each placed row is assembled in one
+    // L2 (write-back stores) before it goes to HBM: 113.3 against 116.5 us
+    // for the whole dispatch at T = 4096, H = 7168 on MI355X.
+    const unsigned nb = gridDim.x, per = nb >> 3, rem = nb & 7;
+    const unsigned xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const unsigned lb = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    const int t = (int)(lb / (unsigned)a.hchunks);
+    const int c = (int)(lb - (unsigned)t * (unsigned)a.hchunks);
     const int nvec = a.H / 8;
     const int nt = blockDim.x;
     du32x4 v[V];
