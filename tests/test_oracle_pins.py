@@ -9,6 +9,7 @@ operand, wrong rounding or tie rule) would break.
 """
 import math
 import os
+import re
 from fractions import Fraction
 
 import numpy as np
@@ -736,3 +737,237 @@ def test_dispatch_then_combine_is_identity_and_counts_accumulate():
     np.testing.assert_array_equal(counts2, 2 * counts)
     with pytest.raises(oracle.OracleError):
         oracle.dispatch(x, np.full((T, 1), E, np.int32), E, ep, 64)
+
+
+# ------------------------------------------------- non-finite values
+#
+# The pages fix the bf16 output and the MX formats but say nothing of NaN or
+# infinity; the reading taken (a NaN or inf block gets the UE8M0 NaN byte
+# 0xFF, its codes taken at e = 0; bf16 rounding keeps NaN a NaN and rounds
+# past the largest finite value to infinity) is pinned here against
+# hand-worked fixtures and torch's CPU bf16 cast. The sign and payload of a
+# NaN result are not fixed (IEEE 754 leaves them open), so NaN outputs are
+# compared as "is a NaN" only.
+
+_REP = re.compile(r"\{([^}]*)\}\*(\d+)")
+
+
+def _fnum(tok):
+    t = tok.strip()
+    if t in ("inf", "+inf"):
+        return math.inf
+    if t == "-inf":
+        return -math.inf
+    return _num(t)
+
+
+def load_nonfinite(name):
+    """Parser of the non-finite fixtures (grammar stated in their headers)."""
+    fx = {"rows": [], "rowfill": {}, "slots": {}, "expect": {}, "residual": [],
+          "residualfill": {}, "expect_residual": {}, "cases": [],
+          "mx8_scales": {}, "mx8_codes": {}, "mx4_scales": {}, "mx4_codes": {}}
+    cur = fx
+    for raw in open(os.path.join(GOLDEN, name)):
+        line = raw.split("#", 1)[0].strip()
+        if not line:
+            continue
+        head, _, body = line.partition(":")
+        hs = head.split()
+        at = 0
+        if len(hs) > 1 and hs[-1].startswith("@"):
+            at, hs = int(hs[-1][1:]), hs[:-1]
+        toks = _REP.sub(lambda m: " ".join([m.group(1)] * int(m.group(2))), body).split()
+        key = hs[0]
+        if key == "dims":
+            fx["dims"] = {kv.split("=")[0]: int(kv.split("=")[1]) for kv in hs[1:]}
+        elif key == "case":
+            cur = {"name": hs[1], "expect_norm": {}, "mx8_scales": {}, "mx8_codes": {}}
+            for kv in hs[2:]:
+                cur[kv.split("=")[0]] = float(kv.split("=")[1])
+            fx["cases"].append(cur)
+        elif key == "row":
+            fx["rows"].append(((int(hs[1]), int(hs[2])), at, [_fnum(v) for v in toks]))
+        elif key == "rowfill":
+            fx["rowfill"][(int(hs[1]), int(hs[2]))] = _fnum(toks[0])
+        elif key == "slot":
+            fx["slots"][(int(hs[1]), int(hs[2]))] = (int(toks[0]), int(toks[1]), _fnum(toks[2]))
+        elif key == "residual":
+            fx["residual"].append((int(hs[1]), at, [_fnum(v) for v in toks]))
+        elif key == "residualfill":
+            fx["residualfill"][int(hs[1])] = _fnum(toks[0])
+        elif key == "gamma":
+            fx["gamma"] = [_fnum(v) for v in toks]
+        elif key in ("expect", "expect_residual", "expect_norm"):
+            tgt = cur if key == "expect_norm" else fx
+            tgt[key].setdefault(int(hs[1]), []).append((at, [_fnum(v) for v in toks]))
+        elif key in ("mx8_scales", "mx4_scales"):
+            cur[key][int(hs[1])] = [int(v) for v in toks]
+        elif key in ("mx8_codes", "mx4_codes"):
+            cur[key].setdefault(int(hs[1]), []).append((at, toks))
+        else:
+            raise ValueError(raw)
+    return fx
+
+
+def _exact_bf16(vals):
+    """bf16 bits of hand values that bf16 must hold exactly (NaN aside)."""
+    v = np.asarray(vals, dtype=np.float64)
+    b = to_bf16_bits(v)
+    fin = ~np.isnan(v)
+    np.testing.assert_array_equal(bf16_to_f32(b)[fin].astype(np.float64), v[fin],
+                                  err_msg="fixture value not exact in bf16")
+    return b
+
+
+def _placed(entries, n, fill=0.0):
+    """Row of n values from (offset, values) pieces over a fill value."""
+    row = np.full(n, fill, dtype=np.float64)
+    for at, vals in entries:
+        row[at:at + len(vals)] = vals
+    return row
+
+
+def nonfinite_arrays(fx):
+    """payload bf16 bits, src_info, weights (and residual, gamma if given)."""
+    d = fx["dims"]
+    pay = np.zeros((d["ep"], d["mtpr"], d["H"]), np.float64)
+    for (r, i), v in fx["rowfill"].items():
+        pay[r, i] = v
+    for (r, i), at, vals in fx["rows"]:
+        pay[r, i, at:at + len(vals)] = vals
+    payload = _exact_bf16(pay.reshape(-1)).reshape(pay.shape)
+    src = np.full((d["T"], d["k"], 2), -1, np.int32)
+    w = np.zeros((d["T"], d["k"]), np.float32)
+    for (t, j), (r, row, wj) in fx["slots"].items():
+        src[t, j] = (r, row)
+        w[t, j] = np.float32(wj)
+        assert float(w[t, j]) == wj, "weight not exact in fp32"
+    res = gam = None
+    if fx["residualfill"] or fx["residual"]:
+        res = np.zeros((d["T"], d["H"]), np.float64)
+        for t, v in fx["residualfill"].items():
+            res[t] = v
+        for t, at, vals in fx["residual"]:
+            res[t, at:at + len(vals)] = vals
+        res = _exact_bf16(res.reshape(-1)).reshape(res.shape)
+        gam = _exact_bf16(fx["gamma"])
+    return payload, src, w, res, gam
+
+
+def assert_bf16_expect(got, entries, H, what):
+    """Exact bits where a number is expected (signed zeros included), any NaN
+    where "nan" is expected."""
+    exp = _placed(entries, H)
+    nan = np.isnan(exp)
+    got_nan = (got & 0x7FFF) > 0x7F80
+    np.testing.assert_array_equal(got_nan, nan, err_msg=f"{what}: NaN positions")
+    np.testing.assert_array_equal(got[~nan], to_bf16_bits(exp[~nan]), err_msg=what)
+
+
+def assert_codes_expect(got, entries, n, width, what):
+    """e4m3 bytes (width 8) or e2m1 nibbles (width 4); "nn" / "n" accept the
+    NaN-block code 0x7F / 7 with either sign; unset entries expect code 0."""
+    exp = ["0"] * n
+    for at, toks in entries:
+        exp[at:at + len(toks)] = toks
+    mag = 0x7F if width == 8 else 0x7
+    for i, (g, e) in enumerate(zip(got, exp)):
+        if e.strip("n") == "":
+            assert int(g) & mag == mag, f"{what}[{i}]: {int(g):#x}, expected a NaN code"
+        else:
+            assert int(g) == int(e, 16), f"{what}[{i}]: {int(g):#x} != {e}"
+
+
+def _unpack_e2m1(packed):
+    p = packed.astype(np.uint8)
+    return np.stack([p & 0xF, p >> 4], axis=-1).reshape(p.shape[0], -1)
+
+
+def test_golden_nonfinite_combine():
+    """NaN / +-inf blocks of the MX outputs take byte 0xFF and codes at e = 0;
+    bf16 keeps NaN, rounds the halfway point above the largest bf16 to inf
+    and the point just below it to 0x7F7F."""
+    fx = load_nonfinite("nonfinite_combine_small.txt")
+    d = fx["dims"]
+    payload, src, w, _, _ = nonfinite_arrays(fx)
+    out = oracle.combine(payload, src, w)
+    c8, s8 = oracle.combine_mxfp8(payload, src, w)
+    c4, s4 = oracle.combine_mxfp4(payload, src, w)
+    n4 = _unpack_e2m1(c4)
+    for t in range(d["T"]):
+        assert_bf16_expect(out[t], fx["expect"].get(t, []), d["H"], f"bf16 token {t}")
+        assert list(s8[t]) == fx["mx8_scales"][t], f"mxfp8 scales token {t}"
+        assert_codes_expect(c8[t], fx["mx8_codes"].get(t, []), d["H"], 8, f"e4m3 token {t}")
+        assert list(s4[t]) == fx["mx4_scales"][t], f"mxfp4 scales token {t}"
+        assert_codes_expect(n4[t], fx["mx4_codes"].get(t, []), d["H"], 4, f"e2m1 token {t}")
+
+
+def test_golden_nonfinite_rmsnorm():
+    """NaN and inf in the residual: IEEE propagation through the statistic
+    (NaN row; inf -> rstd = +0, signed zeros, inf * 0 = NaN), and the MXFP8
+    copy of the normalised row follows the NaN-block rule."""
+    fx = load_nonfinite("nonfinite_rmsnorm_small.txt")
+    d = fx["dims"]
+    payload, src, w, res, gam = nonfinite_arrays(fx)
+    assert [c["name"] for c in fx["cases"]] == ["wb0", "wb1"]
+    for case in fx["cases"]:
+        eps, wb = case["eps"], case["weight_bias"]
+        ro, no = oracle.combine_residual_rmsnorm(payload, src, w, None, res, gam, eps, wb)
+        ro2, no2, codes, scales = oracle.combine_residual_rmsnorm_mxfp8(
+            payload, src, w, None, res, gam, eps, wb)
+        for t in range(d["T"]):
+            for got in (ro[t], ro2[t]):
+                assert_bf16_expect(got, fx["expect_residual"][t], d["H"], f"residual_out {t}")
+            for got in (no[t], no2[t]):
+                assert_bf16_expect(got, case["expect_norm"][t], d["H"],
+                                   f"norm_out {case['name']} token {t}")
+            assert list(scales[t]) == case["mx8_scales"][t], f"scales {case['name']} {t}"
+            assert_codes_expect(codes[t], case["mx8_codes"][t], d["H"], 8,
+                                f"codes {case['name']} {t}")
+
+
+def test_bf16_rounding_matches_torch_including_nonfinite():
+    """oracle_bf16_rne against torch's CPU float -> bfloat16 cast (round to
+    nearest even) on every bf16 value with the low half at the rounding
+    boundaries, the fp32 extremes and random fp32 patterns: identical bits
+    for every non-NaN input (inf, overflow to inf, subnormals, signed zeros);
+    a quiet NaN for every NaN input."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    rng = np.random.default_rng(31)
+    bits = np.concatenate([(hi[:, None] | lows[None, :]).reshape(-1),
+                           rng.integers(0, 1 << 32, 200_000, dtype=np.uint64).astype(np.uint32),
+                           np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF, 0xFF7F8000,
+                                     0x7F800000, 0xFF800000, 0x00000001, 0x80000001,
+                                     0x00FF8000, 0x7FC00000, 0xFFC00000, 0x7F800001],
+                                    np.uint32)])
+    f = bits.view(np.float32)
+    got = np.array([oracle.bf16_rne(float(v)) for v in f], dtype=np.uint16)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(f)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert ((got[nan] & 0x7FC0) == 0x7FC0).all(), "NaN must stay a quiet NaN"
+    # the cases the fixtures work by hand, by value
+    assert oracle.bf16_rne(float(np.uint32(0x7F7F8000).view(np.float32))) == 0x7F80
+    assert oracle.bf16_rne(float(np.uint32(0x7F7F7FFF).view(np.float32))) == 0x7F7F
+    assert oracle.bf16_rne(math.inf) == 0x7F80 and oracle.bf16_rne(-math.inf) == 0xFF80
+
+
+def test_reduce_dense_nonfinite_equals_combine_with_identity_map():
+    """NaN, +-inf and values near the bf16 limit in the inputs, the token
+    input and the residual: the local reduce gives the bits of the pinned
+    combine through the identity slot map."""
+    x, sc, tok, res, gam, ident = _dense_case(3)
+    rng = np.random.default_rng(4)
+    special = to_bf16_bits([np.nan, np.inf, -np.inf, 3.3e38, -3.3e38])
+    for arr in (x.reshape(-1), tok.reshape(-1), res.reshape(-1)):
+        pos = rng.choice(arr.size, size=max(4, arr.size // 200), replace=False)
+        arr[pos] = special[rng.integers(0, special.size, pos.size)]
+    for s_, t_ in [(sc, tok), (None, None), (None, tok)]:
+        np.testing.assert_array_equal(oracle.reduce_dense(x, s_, t_),
+                                      oracle.combine(x, ident, s_, t_))
+    for wb in (0.0, 1.0):
+        ro, no = oracle.reduce_dense(x, sc, tok, res, gam, 1e-6, wb)
+        ro2, no2 = oracle.combine_residual_rmsnorm(x, ident, sc, tok, res, gam, 1e-6, wb)
+        np.testing.assert_array_equal(ro, ro2)
+        np.testing.assert_array_equal(no, no2)
