@@ -72,14 +72,17 @@ def strip_comments(src):
     return " ".join("".join(out).split())
 
 
+KERNEL_SOURCES = ("combine_kernels.h", "dispatch_kernels.h", "moe_combine.hip")
+
+
 def kernel_source_hash():
-    """sha256 over the kernel and ABI sources, comments left out; byte
-    counters taken from other kernel code are not reported."""
+    """sha256 over the device code and the launch planning (what decides the
+    bytes a launch moves), comments left out; byte counters taken from other
+    kernel code are not reported."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_expert_combine_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
-    files.append(os.path.join(ROOT, "include", "moe_combine.h"))
+    files = [os.path.join(csrc, f) for f in KERNEL_SOURCES]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, encoding="utf-8") as fh:

@@ -50,8 +50,10 @@
  *  - shared_out: [num_tokens, hidden] bf16, or NULL. It is added unweighted,
  *    after the routed sum.
  *  - Outputs have at least num_tokens rows. Exactly the first num_tokens
- *    rows are written; rows past them are untouched. Outputs must not
- *    overlap any input, except where an entry point allows it.
+ *    rows are written; rows past them are untouched. No byte of an output's
+ *    first num_tokens rows may lie in an input or in another output (the
+ *    payload counts with all its ep_size * max_tokens_per_rank rows), except
+ *    where an entry point allows it; a call that breaks this is rejected.
  *  - hidden must be a positive multiple of 8 (16-byte rows), at most 2^28
  *    (output rows are addressed with 32-bit byte offsets). bf16 pointers
  *    must be 16-byte aligned, src_info 8-byte aligned, router_weights 4-byte
@@ -79,7 +81,79 @@ typedef enum {
     MOE_ERR_HIP = 3
 } moe_status_t;
 
-#define MOE_COMBINE_ABI_VERSION 1
+#define MOE_COMBINE_ABI_VERSION 2
+
+/* Entry-point kinds, for moe_combine_check_args and
+ * moe_combine_describe_launch. */
+enum {
+    MOE_KIND_COMBINE = 0,                        /* moe_combine */
+    MOE_KIND_COMBINE_RESIDUAL_RMSNORM = 1,       /* moe_combine_residual_rmsnorm */
+    MOE_KIND_COMBINE_MXFP8 = 2,                  /* moe_combine_mxfp8 */
+    MOE_KIND_COMBINE_RESIDUAL_RMSNORM_MXFP8 = 3, /* moe_combine_residual_rmsnorm_mxfp8 */
+    MOE_KIND_COMBINE_MXFP4 = 4,                  /* moe_combine_mxfp4 */
+    MOE_KIND_DISPATCH = 5,                       /* moe_dispatch */
+    MOE_KIND_REDUCE_DENSE = 6,                   /* moe_reduce_dense */
+    MOE_KIND_REDUCE_DENSE_RESIDUAL_RMSNORM = 7   /* moe_reduce_dense_residual_rmsnorm */
+};
+
+/* The arguments of one entry-point call, by the entry point's parameter
+ * names. A kind reads the fields its entry point takes and ignores the
+ * rest (leave them zero). For MOE_KIND_DISPATCH, payload and src_info are
+ * the call's outputs. */
+typedef struct moe_call_args {
+    int32_t kind;                   /* MOE_KIND_* */
+    int32_t hidden;
+    int64_t num_tokens;
+    int32_t top_k;                  /* combine kinds, dispatch */
+    int32_t ep_size;                /* combine kinds, dispatch */
+    int64_t max_tokens_per_rank;    /* combine kinds, dispatch */
+    int32_t n_in;                   /* local-reduce kinds */
+    int32_t num_experts;            /* dispatch */
+    float eps;                      /* RMSNorm kinds */
+    float weight_bias;              /* RMSNorm kinds (any value is valid) */
+    const void *payload;
+    const int32_t *src_info;
+    const float *router_weights;
+    const void *shared_out;
+    const void *inputs;             /* local-reduce kinds */
+    const float *scales;            /* local-reduce kinds */
+    const void *token_input;        /* local-reduce kinds */
+    const void *residual_in;
+    const void *gamma;
+    const void *x;                  /* dispatch */
+    const int32_t *topk_ids;        /* dispatch */
+    void *out;                      /* moe_combine, moe_reduce_dense */
+    void *residual_out;
+    void *norm_out;
+    void *out_fp8;
+    void *out_fp4;
+    uint8_t *out_scales;
+    int32_t *recv_counts;           /* dispatch */
+    void *workspace;                /* dispatch */
+    size_t workspace_bytes;         /* dispatch */
+} moe_call_args_t;
+
+/*
+ * Validates the arguments of one call without touching the GPU: pure host
+ * code, no HIP call, no allocation. Every entry point runs exactly this
+ * validation before its first HIP call, so MOE_OK here means the entry
+ * point will not reject these arguments (a MOE_COMBINE_TILE override can
+ * still make a launch shape unsupported). It checks:
+ *  - sizes (the ranges stated with each entry point);
+ *  - required pointers, for num_tokens > 0 (num_tokens == 0 needs none);
+ *  - alignment;
+ *  - byte ranges: every output's written range (first num_tokens rows) must
+ *    not intersect an input's range or another output's, except
+ *    residual_out == residual_in exactly.
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG, or MOE_ERR_UNSUPPORTED (an RMSNorm
+ * row longer than 32768); moe_combine_last_error() names the argument.
+ * Sources: flashinfer.comm.moe_a2a_combine, Parameters output (a contiguous
+ * caller-provided output of matching shape and dtype on the same device);
+ * flashinfer.megamoe.nvfp4_mega_moe, Parameters y (the first num_tokens
+ * rows are written in place) and Notes (contiguous tensors on one device);
+ * flashinfer.comm.trtllm_moe_allreduce_fusion, Parameters residual_out.
+ */
+moe_status_t moe_combine_check_args(const moe_call_args_t *args);
 
 /* Version of this ABI (MOE_COMBINE_ABI_VERSION). */
 int moe_combine_abi_version(void);
@@ -305,8 +379,8 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids,
 
 /*
  * Describes the launch an entry point would make for these sizes, without
- * touching the GPU. kind: 0 = moe_combine, 1 = residual + RMSNorm,
- * 2 = MXFP8, 3 = residual + RMSNorm + MXFP8, 4 = MXFP4, 5 = moe_dispatch.
+ * touching the GPU. kind is a MOE_KIND_* value; for the local-reduce kinds
+ * top_k is n_in.
  *
  * On success, writes a NUL-terminated text into buf, such as
  * "threads=128 vec_per_thread=1 chunks=7 blocks=28672 slot_tile=8 masked=0"

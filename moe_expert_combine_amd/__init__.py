@@ -28,8 +28,28 @@ __all__ = ["moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
            "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
            "moe_reduce_dense", "moe_reduce_dense_residual_rmsnorm",
            "moe_dispatch", "dispatch_workspace_size",
-           "describe_launch", "abi_version", "lib", "library_path",
-           "MoeCombineError"]
+           "describe_launch", "check_args", "CallArgs", "KIND", "abi_version", "lib",
+           "library_path", "MoeCombineError"]
+
+# Entry-point kinds (MOE_KIND_* in include/moe_combine.h).
+KIND = {"combine": 0, "combine_residual_rmsnorm": 1, "combine_mxfp8": 2,
+        "combine_residual_rmsnorm_mxfp8": 3, "combine_mxfp4": 4, "dispatch": 5,
+        "reduce_dense": 6, "reduce_dense_residual_rmsnorm": 7}
+
+
+class CallArgs(ctypes.Structure):
+    """moe_call_args_t: the arguments of one entry-point call, by name
+    (pointers as integers, sizes as ints)."""
+    _fields_ = [("kind", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_tokens", ctypes.c_int64), ("top_k", ctypes.c_int32),
+                ("ep_size", ctypes.c_int32), ("max_tokens_per_rank", ctypes.c_int64),
+                ("n_in", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("weight_bias", ctypes.c_float)] + [
+        (n, ctypes.c_void_p) for n in (
+            "payload", "src_info", "router_weights", "shared_out", "inputs", "scales",
+            "token_input", "residual_in", "gamma", "x", "topk_ids", "out", "residual_out",
+            "norm_out", "out_fp8", "out_fp4", "out_scales", "recv_counts", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t)]
 
 library_path = _build.LIB
 
@@ -46,9 +66,13 @@ _lib = None
 
 
 def _load():
-    """Load the library; build it first only if no build exists."""
-    if not os.path.exists(_build.LIB):
+    """Load the library. If it is missing, or was built from other sources
+    than the ones in the tree, rebuild it first; if that fails, raise:
+    a stale binary is never loaded."""
+    if _build.stale():
         _build.build()
+        if _build.stale():
+            raise RuntimeError(f"{_build.LIB} does not match its sources after a rebuild")
     L = ctypes.CDLL(_build.LIB)
     P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     dims = [I64, I32, I32, I32, I64, P]
@@ -68,6 +92,8 @@ def _load():
     for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
               "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4"):
         getattr(L, f).restype = ctypes.c_int
+    L.moe_combine_check_args.argtypes = [ctypes.POINTER(CallArgs)]
+    L.moe_combine_check_args.restype = ctypes.c_int
     L.moe_combine_describe_launch.argtypes = [ctypes.c_int, I64, I32, I32, ctypes.c_char_p, I32]
     L.moe_combine_describe_launch.restype = ctypes.c_int
     L.moe_combine_abi_version.argtypes = []
@@ -100,9 +126,21 @@ def abi_version() -> int:
     return lib().moe_combine_abi_version()
 
 
+def check_args(kind, **fields):
+    """moe_combine_check_args: validate one call's arguments on the host
+    (sizes, required pointers, alignment, byte-range overlap) without
+    touching the GPU. ``kind`` is a name of KIND or its number; fields are
+    the entry point's parameter names (pointers as ints). Returns the status
+    and the library's message."""
+    a = CallArgs(kind=KIND.get(kind, kind) if isinstance(kind, str) else kind, **fields)
+    st = lib().moe_combine_check_args(ctypes.byref(a))
+    return st, lib().moe_combine_last_error().decode()
+
+
 def describe_launch(kind: int, num_tokens: int, hidden: int, top_k: int) -> str:
-    """Launch shape an entry point would use (kind 0 bf16, 1 RMSNorm, 2 MXFP8,
-    3 RMSNorm + MXFP8, 4 MXFP4)."""
+    """Launch shape an entry point would use (kind as in KIND: 0 bf16,
+    1 RMSNorm, 2 MXFP8, 3 RMSNorm + MXFP8, 4 MXFP4, 5 dispatch, 6 and 7 the
+    local reduce, with top_k = n_in)."""
     buf = ctypes.create_string_buffer(256)
     _check("moe_combine_describe_launch",
            lib().moe_combine_describe_launch(kind, num_tokens, hidden, top_k, buf, 256))

@@ -1,48 +1,34 @@
-// Host side of the MoE expert-combine library: argument validation, launch
-// planning, kernel dispatch and the C ABI declared in include/moe_combine.h.
-//
-// Validation is pure host code and runs before any HIP call, so argument
-// errors are reported identically on machines without a GPU. The library
-// allocates nothing, keeps no state between calls and never synchronises.
+// Host side of the MoE expert-combine library: launch planning, kernel
+// dispatch and the compute entry points of the C ABI declared in
+// include/moe_combine.h. Argument validation (check_args.cpp) is pure host
+// code and runs before any HIP call, so argument errors are reported
+// identically on machines without a GPU. The library allocates nothing,
+// keeps no state between calls and never synchronises.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
-#include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include "moe_combine.h"
+#include "host_check.h"
 #include "combine_kernels.h"
 #include "dispatch_kernels.h"
 
 namespace {
 
-thread_local char g_err[256] = "";
+using moe_host::fail;
+using moe_host::ok;
 
-moe_status_t fail(moe_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-moe_status_t fail(moe_status_t st, const char *fmt, ...) {
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(g_err, sizeof g_err, fmt, ap);
-    va_end(ap);
-    return st;
-}
+static_assert(moe::kChunk == moe_host::kDispatchChunk, "dispatch chunk size");
+static_assert(moe::kMaxExperts == moe_host::kMaxExperts, "dispatch expert limit");
 
-moe_status_t ok() {
-    g_err[0] = '\0';
-    return MOE_OK;
-}
-
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-constexpr int kMaxTopK = 32;
 constexpr int64_t kPlaceMaxPairs = 1 << 16;   // one-kernel dispatch placement up to here (measured crossover)
 constexpr int kMaxThreads = 1024;
-constexpr int kMaxRmsHidden = 512 * 8 * 8;   // 512 threads x 8 vectors x 8 bf16
-constexpr int kMaxHidden = 1 << 28;           // output rows are addressed with 32-bit byte offsets
+static_assert(moe_host::kMaxRmsHidden <= 512 * 8 * 8, "RMSNorm rows: 512 threads x 8 vectors x 8 bf16");
 
 // Launch shape of one call.
 struct Plan {
@@ -110,6 +96,8 @@ void launch_scatter(int vec, dim3 grid, dim3 block, hipStream_t s, const moe::Di
     }
 }
 
+int64_t dispatch_chunks(int64_t T, int32_t k) { return (T * k + moe::kChunk - 1) / moe::kChunk; }
+
 moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
     const int nvec = H / 8;
     p->kt = k <= 2 ? 2 : (k <= 4 ? 4 : 8);
@@ -128,7 +116,8 @@ moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
                     break;
                 }
             }
-            if (!vec) return fail(MOE_ERR_UNSUPPORTED, "hidden %d too large for the RMSNorm epilogue (max %d)", H, kMaxRmsHidden);
+            if (!vec) return fail(MOE_ERR_UNSUPPORTED, "hidden %d too large for the RMSNorm epilogue (max %d)", H,
+                                  moe_host::kMaxRmsHidden);
         }
         if ((int64_t)threads * vec < nvec)
             return fail(MOE_ERR_UNSUPPORTED, "tile %dx%d does not cover hidden %d for RMSNorm", threads, vec, H);
@@ -157,26 +146,6 @@ moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
     p->masked = (int64_t)p->chunks * threads * vec != nvec;
     p->blocks = T * (int64_t)p->chunks;
     if (p->blocks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large (%lld workgroups)", (long long)p->blocks);
-    return MOE_OK;
-}
-
-moe_status_t check_common(const void *payload, const int32_t *src_info, const float *w, const void *shared,
-                          int64_t T, int32_t H, int32_t k, int32_t ep, int64_t mtpr) {
-    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %lld)", (long long)T);
-    if (H <= 0 || H % 8) return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", H);
-    if (H > kMaxHidden) return fail(MOE_ERR_INVALID_ARG, "hidden must be <= %d (got %d)", kMaxHidden, H);
-    if (k < 1 || k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, %d] (got %d)", kMaxTopK, k);
-    if (ep < 1) return fail(MOE_ERR_INVALID_ARG, "ep_size must be >= 1 (got %d)", ep);
-    if (mtpr < 1 || mtpr > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "max_tokens_per_rank must be in [1, 2^31) (got %lld)", (long long)mtpr);
-    if (T > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be < 2^31");
-    if ((double)ep * (double)mtpr * (double)H * 2.0 > 9.0e18) return fail(MOE_ERR_INVALID_ARG, "payload size overflows");
-    if (T == 0) return MOE_OK;
-    if (!payload) return fail(MOE_ERR_INVALID_ARG, "payload is NULL");
-    if (!src_info) return fail(MOE_ERR_INVALID_ARG, "src_info is NULL");
-    if (!aligned(payload, 16)) return fail(MOE_ERR_INVALID_ARG, "payload must be 16-byte aligned");
-    if (!aligned(src_info, 8)) return fail(MOE_ERR_INVALID_ARG, "src_info must be 8-byte aligned");
-    if (w && !aligned(w, 4)) return fail(MOE_ERR_INVALID_ARG, "router_weights must be 4-byte aligned");
-    if (shared && !aligned(shared, 16)) return fail(MOE_ERR_INVALID_ARG, "shared_out must be 16-byte aligned");
     return MOE_OK;
 }
 
@@ -238,36 +207,64 @@ moe::KernelArgs base_args(const void *payload, const int32_t *src_info, const fl
     return a;
 }
 
+// The arguments of a combine-kind call, for the validator.
+moe_call_args_t combine_call(int kind, const void *payload, const int32_t *src_info, const float *w,
+                             const void *shared, int64_t T, int32_t H, int32_t k, int32_t ep, int64_t mtpr) {
+    moe_call_args_t c;
+    memset(&c, 0, sizeof c);
+    c.kind = kind;
+    c.payload = payload;
+    c.src_info = src_info;
+    c.router_weights = w;
+    c.shared_out = shared;
+    c.num_tokens = T;
+    c.hidden = H;
+    c.top_k = k;
+    c.ep_size = ep;
+    c.max_tokens_per_rank = mtpr;
+    return c;
+}
+
+moe_call_args_t reduce_call(int kind, const void *inputs, int32_t n_in, const float *scales,
+                            const void *token_input, int64_t T, int32_t H) {
+    moe_call_args_t c;
+    memset(&c, 0, sizeof c);
+    c.kind = kind;
+    c.inputs = inputs;
+    c.n_in = n_in;
+    c.scales = scales;
+    c.token_input = token_input;
+    c.num_tokens = T;
+    c.hidden = H;
+    return c;
+}
+
+// Validation, then the launch plan; MOE_OK with *skip set means nothing to do.
+moe_status_t prepare(const moe_call_args_t &c, int epi, int32_t k, Plan *p, bool *skip) {
+    *skip = false;
+    moe_status_t st = moe_host::check_call(c);
+    if (st != MOE_OK) return st;
+    if (c.num_tokens == 0) {
+        *skip = true;
+        return ok();
+    }
+    return make_plan(epi, c.num_tokens, c.hidden, k, p);
+}
+
 }  // namespace
 
 extern "C" {
 
-int moe_combine_abi_version(void) { return MOE_COMBINE_ABI_VERSION; }
-
-const char *moe_combine_status_string(int status) {
-    switch (status) {
-        case MOE_OK: return "MOE_OK";
-        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
-        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
-        case MOE_ERR_HIP: return "MOE_ERR_HIP";
-        default: return "MOE_ERR_UNKNOWN";
-    }
-}
-
-const char *moe_combine_last_error(void) { return g_err; }
-
 moe_status_t moe_combine(const void *payload, const int32_t *src_info, const float *router_weights,
                          const void *shared_out, void *out, int64_t num_tokens, int32_t hidden, int32_t top_k,
                          int32_t ep_size, int64_t max_tokens_per_rank, void *stream) {
-    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
-                                   ep_size, max_tokens_per_rank);
-    if (st != MOE_OK) return st;
-    if (num_tokens == 0) return ok();
-    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
-    if (!aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "out must be 16-byte aligned");
-    if (out == payload || out == shared_out) return fail(MOE_ERR_INVALID_ARG, "out must not alias an input");
+    moe_call_args_t c = combine_call(MOE_KIND_COMBINE, payload, src_info, router_weights, shared_out, num_tokens,
+                                     hidden, top_k, ep_size, max_tokens_per_rank);
+    c.out = out;
     Plan p;
-    if ((st = make_plan(moe::EPI_BF16, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    bool skip;
+    moe_status_t st = prepare(c, moe::EPI_BF16, top_k, &p, &skip);
+    if (st != MOE_OK || skip) return st;
     moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
     a.out0 = out;
     return launch<moe::EPI_BF16>(p, a, stream);
@@ -278,22 +275,18 @@ moe_status_t moe_combine_residual_rmsnorm(const void *payload, const int32_t *sr
                                           float eps, float weight_bias, void *residual_out, void *norm_out,
                                           int64_t num_tokens, int32_t hidden, int32_t top_k, int32_t ep_size,
                                           int64_t max_tokens_per_rank, void *stream) {
-    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
-                                   ep_size, max_tokens_per_rank);
-    if (st != MOE_OK) return st;
+    moe_call_args_t c = combine_call(MOE_KIND_COMBINE_RESIDUAL_RMSNORM, payload, src_info, router_weights,
+                                     shared_out, num_tokens, hidden, top_k, ep_size, max_tokens_per_rank);
+    c.residual_in = residual_in;
+    c.gamma = gamma;
+    c.eps = eps;
+    c.weight_bias = weight_bias;
+    c.residual_out = residual_out;
+    c.norm_out = norm_out;
     Plan p;
-    if ((st = make_plan(moe::EPI_RMSNORM, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
-    if (num_tokens == 0) return ok();
-    if (!residual_in || !gamma || !residual_out || !norm_out)
-        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out are required");
-    if (!aligned(residual_in, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) || !aligned(norm_out, 16))
-        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out must be 16-byte aligned");
-    if (norm_out == residual_out || norm_out == residual_in)
-        return fail(MOE_ERR_INVALID_ARG, "norm_out must differ from residual_in and residual_out");
-    const void *outs[2] = {residual_out, norm_out};
-    for (const void *o : outs)
-        if (o == payload || o == shared_out || o == gamma) return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input");
-    if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+    bool skip;
+    moe_status_t st = prepare(c, moe::EPI_RMSNORM, top_k, &p, &skip);
+    if (st != MOE_OK || skip) return st;
     moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
     a.residual = static_cast<const uint16_t *>(residual_in);
     a.gamma = static_cast<const uint16_t *>(gamma);
@@ -308,18 +301,14 @@ moe_status_t moe_combine_mxfp8(const void *payload, const int32_t *src_info, con
                                const void *shared_out, void *out_fp8, uint8_t *out_scales, int64_t num_tokens,
                                int32_t hidden, int32_t top_k, int32_t ep_size, int64_t max_tokens_per_rank,
                                void *stream) {
-    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
-                                   ep_size, max_tokens_per_rank);
-    if (st != MOE_OK) return st;
-    if (hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8 (got %d)", hidden);
-    if (num_tokens == 0) return ok();
-    if (!out_fp8 || !out_scales) return fail(MOE_ERR_INVALID_ARG, "out_fp8 and out_scales are required");
-    if (!aligned(out_fp8, 8)) return fail(MOE_ERR_INVALID_ARG, "out_fp8 must be 8-byte aligned");
-    if (out_fp8 == payload || out_fp8 == shared_out || (const void *)out_scales == payload ||
-        (const void *)out_scales == shared_out || (const void *)out_scales == out_fp8)
-        return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input or each other");
+    moe_call_args_t c = combine_call(MOE_KIND_COMBINE_MXFP8, payload, src_info, router_weights, shared_out,
+                                     num_tokens, hidden, top_k, ep_size, max_tokens_per_rank);
+    c.out_fp8 = out_fp8;
+    c.out_scales = out_scales;
     Plan p;
-    if ((st = make_plan(moe::EPI_MXFP8, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    bool skip;
+    moe_status_t st = prepare(c, moe::EPI_MXFP8, top_k, &p, &skip);
+    if (st != MOE_OK || skip) return st;
     moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
     a.out0 = out_fp8;
     a.out1 = out_scales;
@@ -330,18 +319,14 @@ moe_status_t moe_combine_mxfp4(const void *payload, const int32_t *src_info, con
                                const void *shared_out, void *out_fp4, uint8_t *out_scales, int64_t num_tokens,
                                int32_t hidden, int32_t top_k, int32_t ep_size, int64_t max_tokens_per_rank,
                                void *stream) {
-    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
-                                   ep_size, max_tokens_per_rank);
-    if (st != MOE_OK) return st;
-    if (hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP4 (got %d)", hidden);
-    if (num_tokens == 0) return ok();
-    if (!out_fp4 || !out_scales) return fail(MOE_ERR_INVALID_ARG, "out_fp4 and out_scales are required");
-    if (!aligned(out_fp4, 4)) return fail(MOE_ERR_INVALID_ARG, "out_fp4 must be 4-byte aligned");
-    if (out_fp4 == payload || out_fp4 == shared_out || (const void *)out_scales == payload ||
-        (const void *)out_scales == shared_out || (const void *)out_scales == out_fp4)
-        return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input or each other");
+    moe_call_args_t c = combine_call(MOE_KIND_COMBINE_MXFP4, payload, src_info, router_weights, shared_out,
+                                     num_tokens, hidden, top_k, ep_size, max_tokens_per_rank);
+    c.out_fp4 = out_fp4;
+    c.out_scales = out_scales;
     Plan p;
-    if ((st = make_plan(moe::EPI_MXFP4, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    bool skip;
+    moe_status_t st = prepare(c, moe::EPI_MXFP4, top_k, &p, &skip);
+    if (st != MOE_OK || skip) return st;
     moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
     a.out0 = out_fp4;
     a.out1 = out_scales;
@@ -355,28 +340,20 @@ moe_status_t moe_combine_residual_rmsnorm_mxfp8(const void *payload, const int32
                                                 void *out_fp8, uint8_t *out_scales, int64_t num_tokens,
                                                 int32_t hidden, int32_t top_k, int32_t ep_size,
                                                 int64_t max_tokens_per_rank, void *stream) {
-    moe_status_t st = check_common(payload, src_info, router_weights, shared_out, num_tokens, hidden, top_k,
-                                   ep_size, max_tokens_per_rank);
-    if (st != MOE_OK) return st;
-    if (hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8 (got %d)", hidden);
+    moe_call_args_t c = combine_call(MOE_KIND_COMBINE_RESIDUAL_RMSNORM_MXFP8, payload, src_info, router_weights,
+                                     shared_out, num_tokens, hidden, top_k, ep_size, max_tokens_per_rank);
+    c.residual_in = residual_in;
+    c.gamma = gamma;
+    c.eps = eps;
+    c.weight_bias = weight_bias;
+    c.residual_out = residual_out;
+    c.norm_out = norm_out;
+    c.out_fp8 = out_fp8;
+    c.out_scales = out_scales;
     Plan p;
-    if ((st = make_plan(moe::EPI_RMSNORM_MXFP8, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
-    if (num_tokens == 0) return ok();
-    if (!residual_in || !gamma || !residual_out || !out_fp8 || !out_scales)
-        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out, out_fp8 and out_scales are required");
-    if (!aligned(residual_in, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) ||
-        (norm_out && !aligned(norm_out, 16)) || !aligned(out_fp8, 8))
-        return fail(MOE_ERR_INVALID_ARG, "misaligned residual_in, gamma, residual_out, norm_out or out_fp8");
-    const void *outs[4] = {residual_out, norm_out, out_fp8, out_scales};
-    for (int i = 0; i < 4; ++i) {
-        if (!outs[i]) continue;
-        if (outs[i] == payload || outs[i] == shared_out || outs[i] == gamma)
-            return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input");
-        if (i > 0 && outs[i] == residual_in) return fail(MOE_ERR_INVALID_ARG, "only residual_out may alias residual_in");
-        for (int j = 0; j < i; ++j)
-            if (outs[j] == outs[i]) return fail(MOE_ERR_INVALID_ARG, "outputs must not alias each other");
-    }
-    if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+    bool skip;
+    moe_status_t st = prepare(c, moe::EPI_RMSNORM_MXFP8, top_k, &p, &skip);
+    if (st != MOE_OK || skip) return st;
     moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
     a.residual = static_cast<const uint16_t *>(residual_in);
     a.gamma = static_cast<const uint16_t *>(gamma);
@@ -389,26 +366,14 @@ moe_status_t moe_combine_residual_rmsnorm_mxfp8(const void *payload, const int32
     return launch<moe::EPI_RMSNORM_MXFP8>(p, a, stream);
 }
 
-static moe_status_t check_dense(const void *inputs, int32_t n_in, const float *scales, const void *token_input,
-                                int64_t T, int32_t H) {
-    if (n_in < 1 || n_in > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "n_in must be in [1, %d] (got %d)", kMaxTopK, n_in);
-    moe_status_t st = check_common(inputs, reinterpret_cast<const int32_t *>(16), scales, token_input, T, H, n_in,
-                                   n_in, T > 0 ? T : 1);
-    if (st != MOE_OK) return st;
-    if (T > 0 && !inputs) return fail(MOE_ERR_INVALID_ARG, "inputs is NULL");
-    return MOE_OK;
-}
-
 moe_status_t moe_reduce_dense(const void *inputs, int32_t n_in, const float *scales, const void *token_input,
                               void *out, int64_t num_tokens, int32_t hidden, void *stream) {
-    moe_status_t st = check_dense(inputs, n_in, scales, token_input, num_tokens, hidden);
-    if (st != MOE_OK) return st;
-    if (num_tokens == 0) return ok();
-    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
-    if (!aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "out must be 16-byte aligned");
-    if (out == inputs || out == token_input) return fail(MOE_ERR_INVALID_ARG, "out must not alias an input");
+    moe_call_args_t c = reduce_call(MOE_KIND_REDUCE_DENSE, inputs, n_in, scales, token_input, num_tokens, hidden);
+    c.out = out;
     Plan p;
-    if ((st = make_plan(moe::EPI_BF16, num_tokens, hidden, n_in, &p)) != MOE_OK) return st;
+    bool skip;
+    moe_status_t st = prepare(c, moe::EPI_BF16, n_in, &p, &skip);
+    if (st != MOE_OK || skip) return st;
     moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, num_tokens, p);
     a.out0 = out;
     return launch<moe::EPI_BF16>(p, a, stream);
@@ -418,21 +383,18 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(const void *inputs, int32_t n_in,
                                                const void *token_input, const void *residual_in, const void *gamma,
                                                float eps, float weight_bias, void *residual_out, void *norm_out,
                                                int64_t num_tokens, int32_t hidden, void *stream) {
-    moe_status_t st = check_dense(inputs, n_in, scales, token_input, num_tokens, hidden);
-    if (st != MOE_OK) return st;
+    moe_call_args_t c = reduce_call(MOE_KIND_REDUCE_DENSE_RESIDUAL_RMSNORM, inputs, n_in, scales, token_input,
+                                    num_tokens, hidden);
+    c.residual_in = residual_in;
+    c.gamma = gamma;
+    c.eps = eps;
+    c.weight_bias = weight_bias;
+    c.residual_out = residual_out;
+    c.norm_out = norm_out;
     Plan p;
-    if ((st = make_plan(moe::EPI_RMSNORM, num_tokens, hidden, n_in, &p)) != MOE_OK) return st;
-    if (num_tokens == 0) return ok();
-    if (!residual_in || !gamma || !residual_out || !norm_out)
-        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out are required");
-    if (!aligned(residual_in, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) || !aligned(norm_out, 16))
-        return fail(MOE_ERR_INVALID_ARG, "residual_in, gamma, residual_out and norm_out must be 16-byte aligned");
-    if (norm_out == residual_out || norm_out == residual_in)
-        return fail(MOE_ERR_INVALID_ARG, "norm_out must differ from residual_in and residual_out");
-    const void *outs[2] = {residual_out, norm_out};
-    for (const void *o : outs)
-        if (o == inputs || o == token_input || o == gamma) return fail(MOE_ERR_INVALID_ARG, "outputs must not alias an input");
-    if (!(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "eps must be >= 0");
+    bool skip;
+    moe_status_t st = prepare(c, moe::EPI_RMSNORM, n_in, &p, &skip);
+    if (st != MOE_OK || skip) return st;
     moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, num_tokens, p);
     a.residual = static_cast<const uint16_t *>(residual_in);
     a.gamma = static_cast<const uint16_t *>(gamma);
@@ -443,43 +405,29 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(const void *inputs, int32_t n_in,
     return launch<moe::EPI_RMSNORM>(p, a, stream);
 }
 
-static int64_t dispatch_chunks(int64_t T, int32_t k) { return (T * k + moe::kChunk - 1) / moe::kChunk; }
-
-size_t moe_dispatch_workspace_size(int64_t num_tokens, int32_t top_k, int32_t num_experts, int32_t ep_size,
-                                   int64_t max_tokens_per_rank) {
-    if (num_tokens < 0 || top_k < 1 || num_experts < 1 || ep_size < 1 || max_tokens_per_rank < 1) return 0;
-    // offs [nchunks, E] + local [T * k], int32 (ep_size and capacity are
-    // part of the signature so that the layout may depend on them)
-    const int64_t n = (dispatch_chunks(num_tokens, top_k) * (int64_t)num_experts + num_tokens * top_k) * 4;
-    return (size_t)((n + 255) / 256 * 256);
-}
-
 moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_tokens, int32_t hidden,
                           int32_t top_k, int32_t num_experts, int32_t ep_size, int64_t max_tokens_per_rank,
                           void *payload, int32_t *src_info, int32_t *recv_counts, void *workspace,
                           size_t workspace_bytes, void *stream) {
-    if (num_tokens < 0 || num_tokens > 0x7FFFFFFFLL)
-        return fail(MOE_ERR_INVALID_ARG, "num_tokens must be in [0, 2^31)");
-    if (hidden <= 0 || hidden % 8) return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", hidden);
-    if (top_k < 1 || top_k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, %d] (got %d)", kMaxTopK, top_k);
-    if (num_experts < 1 || num_experts > moe::kMaxExperts)
-        return fail(MOE_ERR_INVALID_ARG, "num_experts must be in [1, %d] (got %d)", moe::kMaxExperts, num_experts);
-    if (ep_size < 1 || num_experts % ep_size)
-        return fail(MOE_ERR_INVALID_ARG, "ep_size must divide num_experts (got %d, %d)", ep_size, num_experts);
-    if (max_tokens_per_rank < 1 || max_tokens_per_rank > 0x7FFFFFFFLL)
-        return fail(MOE_ERR_INVALID_ARG, "max_tokens_per_rank must be in [1, 2^31)");
-    if (num_tokens * (int64_t)top_k > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens * top_k must be < 2^31");
+    moe_call_args_t c;
+    memset(&c, 0, sizeof c);
+    c.kind = MOE_KIND_DISPATCH;
+    c.x = x;
+    c.topk_ids = topk_ids;
+    c.num_tokens = num_tokens;
+    c.hidden = hidden;
+    c.top_k = top_k;
+    c.num_experts = num_experts;
+    c.ep_size = ep_size;
+    c.max_tokens_per_rank = max_tokens_per_rank;
+    c.payload = payload;
+    c.src_info = src_info;
+    c.recv_counts = recv_counts;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace_bytes;
+    moe_status_t st = moe_host::check_call(c);
+    if (st != MOE_OK) return st;
     if (num_tokens == 0) return ok();
-    if (!x || !topk_ids || !payload || !src_info || !workspace)
-        return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, payload, src_info and workspace are required");
-    if (!aligned(x, 16) || !aligned(payload, 16) || !aligned(src_info, 8) || !aligned(topk_ids, 4) ||
-        (recv_counts && !aligned(recv_counts, 4)) || !aligned(workspace, 4))
-        return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x, payload 16 B; src_info 8 B; others 4 B)");
-    const size_t need = moe_dispatch_workspace_size(num_tokens, top_k, num_experts, ep_size, max_tokens_per_rank);
-    if (workspace_bytes < need)
-        return fail(MOE_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
-    if (payload == x || (const void *)src_info == (const void *)topk_ids)
-        return fail(MOE_ERR_INVALID_ARG, "outputs must not alias inputs");
     moe::DispatchArgs a;
     memset(&a, 0, sizeof a);
     a.x = static_cast<const uint16_t *>(x);
@@ -521,13 +469,22 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_to
 
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,
                                          int32_t buflen) {
-    if (kind < 0 || kind > 5) return fail(MOE_ERR_INVALID_ARG, "kind must be in [0, 5]");
+    if (kind < 0 || kind > MOE_KIND_REDUCE_DENSE_RESIDUAL_RMSNORM)
+        return fail(MOE_ERR_INVALID_ARG, "kind must be in [0, 7]");
     if (!buf || buflen < 1) return fail(MOE_ERR_INVALID_ARG, "buf is NULL or empty");
-    if (kind == 5) {
-        if (num_tokens < 0 || num_tokens > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens must be in [0, 2^31)");
-        if (hidden <= 0 || hidden % 8) return fail(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", hidden);
-        if (top_k < 1 || top_k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, %d] (got %d)", kMaxTopK, top_k);
-        if (num_tokens * (int64_t)top_k > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "num_tokens * top_k must be < 2^31");
+    moe_call_args_t c;
+    memset(&c, 0, sizeof c);
+    c.kind = kind;
+    c.num_tokens = num_tokens;
+    c.hidden = hidden;
+    c.top_k = top_k;
+    c.n_in = top_k;
+    c.ep_size = 1;
+    c.max_tokens_per_rank = 1;
+    c.num_experts = 1;
+    moe_status_t st = moe_host::check_sizes(c);
+    if (st != MOE_OK) return st;
+    if (kind == MOE_KIND_DISPATCH) {
         int sthreads = 0, svec = 0;
         dispatch_tile(&sthreads, &svec);
         const int64_t pairs = num_tokens * top_k;
@@ -539,13 +496,10 @@ moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t h
                  (long long)(num_tokens * hchunks));
         return ok();
     }
-    moe_status_t st = check_common(reinterpret_cast<const void *>(16), reinterpret_cast<const int32_t *>(16), nullptr,
-                                   nullptr, num_tokens, hidden, top_k, 1, 1);
-    if (st != MOE_OK) return st;
-    if (kind >= 2 && hidden % 32)
-        return fail(MOE_ERR_INVALID_ARG, "hidden must be a multiple of 32 for MXFP8 / MXFP4");
+    const int epi = kind == MOE_KIND_REDUCE_DENSE ? moe::EPI_BF16
+                    : kind == MOE_KIND_REDUCE_DENSE_RESIDUAL_RMSNORM ? moe::EPI_RMSNORM : kind;
     Plan p;
-    if ((st = make_plan(kind, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
+    if ((st = make_plan(epi, num_tokens, hidden, top_k, &p)) != MOE_OK) return st;
     snprintf(buf, (size_t)buflen, "threads=%d vec_per_thread=%d chunks=%d blocks=%lld slot_tile=%d masked=%d",
              p.threads, p.vec, p.chunks, (long long)p.blocks, p.kt, (int)p.masked);
     return ok();
