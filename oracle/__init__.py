@@ -40,11 +40,18 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# MOE_ORACLE_SANITIZE=1 selects a build with the host AddressSanitizer and
+# UndefinedBehaviorSanitizer (same arithmetic flags); a process that loads it
+# must have libasan preloaded (tests/test_sanitizers.py does this).
+SANITIZE = os.environ.get("MOE_ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 
 GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
            "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o",
            _LIB_PATH, "-lm"]
+SANITIZE_FLAGS = ["-fsanitize=address,undefined,float-cast-overflow",
+                  "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 
 def build(force: bool = False) -> str:
@@ -52,7 +59,7 @@ def build(force: bool = False) -> str:
     if (force or not os.path.exists(_LIB_PATH)
             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        cmd = GCC_CMD[:-3] + ["-o", tmp, "-lm"]
+        cmd = GCC_CMD[:-3] + (SANITIZE_FLAGS if SANITIZE else []) + ["-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
