@@ -42,3 +42,22 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_record_names_its_protocol():
+    """The oracle's CPU baseline: median of three multi-threaded batches, a
+    median of three single-threaded runs, the threads used, the OS core
+    count and the CPU model."""
+    import gen
+    import oracle
+    inp = gen.make_inputs("tiny", 0)
+    run = lambda: oracle.combine(inp.payload, inp.src_info, inp.weights, inp.shared,
+                                 checked=False)
+    rec = bench.time_cpu_oracle(run, inp.T, 394752, 0.3, oracle)
+    assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
+    assert len(rec["batch_tokens_per_s"]) == 3
+    assert sorted(rec["batch_tokens_per_s"])[1] == rec["value"]
+    assert len(rec["single_thread"]["runs_tokens_per_s"]) == 3
+    assert rec["cores"] == rec["omp_threads"] == oracle.max_threads()
+    assert rec["os_cpu_count"] == os.cpu_count() and rec["cpu_model"]
+    assert oracle.max_threads() == rec["omp_threads"]       # threads restored
