@@ -378,6 +378,32 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids,
                           void *stream);
 
 /*
+ * moe_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid allocation. The call allocates nothing. Its
+ * count + scan path keeps its per-chunk expert offsets and per-pair ranks in
+ * the library's own device scratch array of 8 MiB (MOE_DISPATCH_SCRATCH_BYTES),
+ * which each GPU the library runs on holds from the library's load until the
+ * process ends. Arguments, results and errors are those of moe_dispatch.
+ * A call whose count + scan path would need more than 8 MiB of scratch
+ * (dispatch_workspace_size) returns MOE_ERR_UNSUPPORTED; the placement path
+ * (up to 65536 pairs unless MOE_DISPATCH_PATH overrides it) needs none.
+ * Every call on one GPU shares that GPU's scratch array, which keeps the
+ * last call's contents (the kernels overwrite what they read), so calls that
+ * may overlap on one GPU, from any stream or thread, race and must be
+ * ordered by the caller.
+ */
+#define MOE_DISPATCH_SCRATCH_BYTES (8u << 20)
+
+moe_status_t moe_dispatch_noalloc(const void *x, const int32_t *topk_ids,
+                                  int64_t num_tokens, int32_t hidden,
+                                  int32_t top_k, int32_t num_experts,
+                                  int32_t ep_size,
+                                  int64_t max_tokens_per_rank, void *payload,
+                                  int32_t *src_info, int32_t *recv_counts,
+                                  void *stream);
+
+/*
  * Describes the launch an entry point would make for these sizes, without
  * touching the GPU. kind is a MOE_KIND_* value; for the local-reduce kinds
  * top_k is n_in.

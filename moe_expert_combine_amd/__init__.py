@@ -27,7 +27,7 @@ from . import _build
 __all__ = ["moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
            "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4",
            "moe_reduce_dense", "moe_reduce_dense_residual_rmsnorm",
-           "moe_dispatch", "dispatch_workspace_size",
+           "moe_dispatch", "moe_dispatch_noalloc", "dispatch_workspace_size",
            "describe_launch", "check_args", "CallArgs", "KIND", "abi_version", "lib",
            "library_path", "MoeCombineError"]
 
@@ -89,6 +89,8 @@ def _load():
     L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
     L.moe_dispatch.argtypes = [P, P, I64, I32, I32, I32, I32, I64, P, P, P, P, ctypes.c_size_t, P]
     L.moe_dispatch.restype = ctypes.c_int
+    L.moe_dispatch_noalloc.argtypes = [P, P, I64, I32, I32, I32, I32, I64, P, P, P, P]
+    L.moe_dispatch_noalloc.restype = ctypes.c_int
     for f in ("moe_combine", "moe_combine_residual_rmsnorm", "moe_combine_mxfp8",
               "moe_combine_residual_rmsnorm_mxfp8", "moe_combine_mxfp4"):
         getattr(L, f).restype = ctypes.c_int
@@ -392,4 +394,35 @@ def moe_dispatch(x, topk_ids, num_experts, ep_size, max_tokens_per_rank, payload
         _ptr(x), _ptr(topk_ids), T, H, k, num_experts, ep_size, max_tokens_per_rank,
         _ptr(payload), _ptr(src_info), _ptr(recv_counts), _ptr(workspace), workspace.numel(),
         _stream(dev)))
+    return payload, src_info
+
+
+def moe_dispatch_noalloc(x, topk_ids, num_experts, ep_size, payload, src_info, recv_counts=None):
+    """moe_dispatch without a workspace: the library's own device scratch
+    (8 MiB per GPU) holds the count + scan path's intermediates, and nothing
+    is allocated. payload [ep, mtpr, H] and src_info [T, k, 2] are the
+    caller's outputs; recv_counts (int32 [E]) accumulates if given. Calls
+    that may overlap on one GPU race on the shared scratch."""
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(topk_ids, "topk_ids", torch.int32, dev, 2)
+    T, H = x.shape
+    if topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must be [T, top_k]")
+    k = topk_ids.shape[1]
+    _need(payload, "payload", torch.bfloat16, dev, 3)
+    if payload.shape[0] != ep_size or payload.shape[2] != H:
+        raise ValueError(f"payload must be [{ep_size}, max_tokens_per_rank, {H}]")
+    _need(src_info, "src_info", torch.int32, dev, 3)
+    if tuple(src_info.shape) != (T, k, 2):
+        raise ValueError(f"src_info must be [{T}, {k}, 2]")
+    if recv_counts is not None:
+        _need(recv_counts, "recv_counts", torch.int32, dev, 1)
+        if recv_counts.shape[0] != num_experts:
+            raise ValueError(f"recv_counts must be [{num_experts}]")
+    _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
+        _ptr(x), _ptr(topk_ids), T, H, k, num_experts, ep_size, payload.shape[1],
+        _ptr(payload), _ptr(src_info), _ptr(recv_counts), _stream(dev)))
     return payload, src_info

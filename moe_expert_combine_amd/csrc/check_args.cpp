@@ -193,23 +193,27 @@ moe_status_t check_combine_call(const moe_call_args_t &c) {
     return check_overlaps(rd, nr, wr, nw);
 }
 
-moe_status_t check_dispatch_call(const moe_call_args_t &c) {
+// own_scratch: the workspace is the library's own device array (a separate
+// allocation), so the workspace fields are not the caller's and are not
+// checked.
+moe_status_t check_dispatch_call(const moe_call_args_t &c, bool own_scratch) {
     moe_status_t st = check_dispatch_sizes(c);
     if (st != MOE_OK || c.num_tokens == 0) return st;
-    if (!c.x || !c.topk_ids || !c.payload || !c.src_info || !c.workspace)
-        return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, payload, src_info and workspace are required");
+    if (!c.x || !c.topk_ids || !c.payload || !c.src_info || (!own_scratch && !c.workspace))
+        return fail(MOE_ERR_INVALID_ARG, own_scratch ? "x, topk_ids, payload and src_info are required"
+                                                     : "x, topk_ids, payload, src_info and workspace are required");
     if (!aligned(c.x, 16) || !aligned(c.payload, 16) || !aligned(c.src_info, 8) || !aligned(c.topk_ids, 4) ||
-        (c.recv_counts && !aligned(c.recv_counts, 4)) || !aligned(c.workspace, 4))
+        (c.recv_counts && !aligned(c.recv_counts, 4)) || (!own_scratch && !aligned(c.workspace, 4)))
         return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x, payload 16 B; src_info 8 B; others 4 B)");
     const size_t need = dispatch_workspace_bytes(c.num_tokens, c.top_k, c.num_experts);
-    if (c.workspace_bytes < need)
+    if (!own_scratch && c.workspace_bytes < need)
         return fail(MOE_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", c.workspace_bytes, need);
     const uint64_t T = (uint64_t)c.num_tokens, H = (uint64_t)c.hidden, k = (uint64_t)c.top_k;
     const Span rd[2] = {{"x", c.x, T * H * 2}, {"topk_ids", c.topk_ids, T * k * 4}};
     const Span wr[4] = {{"payload", c.payload, (uint64_t)c.ep_size * (uint64_t)c.max_tokens_per_rank * H * 2},
                         {"src_info", c.src_info, T * k * 8},
                         {"recv_counts", c.recv_counts, (uint64_t)c.num_experts * 4},
-                        {"workspace", c.workspace, (uint64_t)need}};
+                        {"workspace", own_scratch ? nullptr : c.workspace, (uint64_t)need}};
     return check_overlaps(rd, 2, wr, 4);
 }
 
@@ -243,10 +247,12 @@ moe_status_t check_sizes(const moe_call_args_t &c) {
 }
 
 moe_status_t check_call(const moe_call_args_t &c) {
-    if (c.kind == MOE_KIND_DISPATCH) return check_dispatch_call(c);
+    if (c.kind == MOE_KIND_DISPATCH) return check_dispatch_call(c, false);
     if (is_combine(c.kind) || is_reduce(c.kind)) return check_combine_call(c);
     return fail(MOE_ERR_INVALID_ARG, "kind must be in [0, 7] (got %d)", c.kind);
 }
+
+moe_status_t check_dispatch_own_scratch(const moe_call_args_t &c) { return check_dispatch_call(c, true); }
 
 }  // namespace moe_host
 

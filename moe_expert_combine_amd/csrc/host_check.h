@@ -26,6 +26,10 @@ moe_status_t ok();
 // overlap between what it writes and everything else it touches).
 moe_status_t check_call(const moe_call_args_t &c);
 
+// The dispatch's checks for the allocation-free entry point, whose
+// workspace is the library's own device array (not checked here).
+moe_status_t check_dispatch_own_scratch(const moe_call_args_t &c);
+
 // Size checks of a kind alone (the launch description validates these).
 moe_status_t check_sizes(const moe_call_args_t &c);
 

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include <stdint.h>
 #include <stdio.h>
@@ -239,6 +240,96 @@ moe_call_args_t reduce_call(int kind, const void *inputs, int32_t n_in, const fl
     return c;
 }
 
+moe_call_args_t dispatch_call(const void *x, const int32_t *topk_ids, int64_t T, int32_t H, int32_t k, int32_t E,
+                              int32_t ep, int64_t mtpr, void *payload, int32_t *src_info, int32_t *recv_counts) {
+    moe_call_args_t c;
+    memset(&c, 0, sizeof c);
+    c.kind = MOE_KIND_DISPATCH;
+    c.x = x;
+    c.topk_ids = topk_ids;
+    c.num_tokens = T;
+    c.hidden = H;
+    c.top_k = k;
+    c.num_experts = E;
+    c.ep_size = ep;
+    c.max_tokens_per_rank = mtpr;
+    c.payload = payload;
+    c.src_info = src_info;
+    c.recv_counts = recv_counts;
+    return c;
+}
+
+// The dispatch's kernels for a validated call with num_tokens > 0; ws holds
+// at least dispatch_workspace_bytes() on the count + scan path.
+moe_status_t dispatch_launch(const moe_call_args_t &c, int32_t *ws, void *stream) {
+    moe::DispatchArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = static_cast<const uint16_t *>(c.x);
+    a.ids = c.topk_ids;
+    a.payload = static_cast<uint16_t *>(const_cast<void *>(c.payload));
+    a.src_info = const_cast<int32_t *>(c.src_info);
+    a.recv_counts = c.recv_counts;
+    a.pairs = c.num_tokens * c.top_k;
+    a.nchunks = (int)dispatch_chunks(c.num_tokens, c.top_k);
+    a.offs = ws;
+    a.local = a.offs + (int64_t)a.nchunks * c.num_experts;
+    a.mtpr = c.max_tokens_per_rank;
+    a.T = (int)c.num_tokens;
+    a.H = c.hidden;
+    a.k = c.top_k;
+    a.E = c.num_experts;
+    a.epr = c.num_experts / c.ep_size;
+    a.segs = std::max(1, std::min(a.nchunks, 1024 / a.epr));
+    a.idbits = 32 - __builtin_clz((unsigned)c.num_experts);
+    int sthreads = 0, svec = 0;
+    dispatch_tile(&sthreads, &svec);
+    a.hchunks = (c.hidden / 8 + sthreads * svec - 1) / (sthreads * svec);
+    if ((int64_t)a.T * a.hchunks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 sg((unsigned)((int64_t)a.T * a.hchunks)), sb(sthreads);
+    if (dispatch_path(a.pairs) == PATH_PLACE) {
+        hipLaunchKernelGGL(moe::dispatch_place, dim3((unsigned)((a.pairs + moe::kPlaceChunk - 1) / moe::kPlaceChunk)),
+                           dim3(moe::kPlace), 0, s, a);
+        launch_scatter<false>(svec, sg, sb, s, a);
+    } else {
+        hipLaunchKernelGGL(moe::dispatch_count, dim3(a.nchunks), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(moe::dispatch_scan, dim3(c.ep_size), dim3(1024), 0, s, a);
+        launch_scatter<true>(svec, sg, sb, s, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// Scratch of the allocation-free dispatch: a file-scope device array that
+// each GPU holds from the library's load until the process ends. On the host
+// its name is only a stand-in for the symbol, not a device address: kernels
+// and copies take the address that hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept.
+constexpr size_t kScratchBytes = MOE_DISPATCH_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+moe_status_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 // Validation, then the launch plan; MOE_OK with *skip set means nothing to do.
 moe_status_t prepare(const moe_call_args_t &c, int epi, int32_t k, Plan *p, bool *skip) {
     *skip = false;
@@ -409,62 +500,35 @@ moe_status_t moe_dispatch(const void *x, const int32_t *topk_ids, int64_t num_to
                           int32_t top_k, int32_t num_experts, int32_t ep_size, int64_t max_tokens_per_rank,
                           void *payload, int32_t *src_info, int32_t *recv_counts, void *workspace,
                           size_t workspace_bytes, void *stream) {
-    moe_call_args_t c;
-    memset(&c, 0, sizeof c);
-    c.kind = MOE_KIND_DISPATCH;
-    c.x = x;
-    c.topk_ids = topk_ids;
-    c.num_tokens = num_tokens;
-    c.hidden = hidden;
-    c.top_k = top_k;
-    c.num_experts = num_experts;
-    c.ep_size = ep_size;
-    c.max_tokens_per_rank = max_tokens_per_rank;
-    c.payload = payload;
-    c.src_info = src_info;
-    c.recv_counts = recv_counts;
+    moe_call_args_t c = dispatch_call(x, topk_ids, num_tokens, hidden, top_k, num_experts, ep_size,
+                                      max_tokens_per_rank, payload, src_info, recv_counts);
     c.workspace = workspace;
     c.workspace_bytes = workspace_bytes;
     moe_status_t st = moe_host::check_call(c);
     if (st != MOE_OK) return st;
     if (num_tokens == 0) return ok();
-    moe::DispatchArgs a;
-    memset(&a, 0, sizeof a);
-    a.x = static_cast<const uint16_t *>(x);
-    a.ids = topk_ids;
-    a.payload = static_cast<uint16_t *>(payload);
-    a.src_info = src_info;
-    a.recv_counts = recv_counts;
-    a.pairs = num_tokens * top_k;
-    a.nchunks = (int)dispatch_chunks(num_tokens, top_k);
-    a.offs = static_cast<int32_t *>(workspace);
-    a.local = a.offs + (int64_t)a.nchunks * num_experts;
-    a.mtpr = max_tokens_per_rank;
-    a.T = (int)num_tokens;
-    a.H = hidden;
-    a.k = top_k;
-    a.E = num_experts;
-    a.epr = num_experts / ep_size;
-    a.segs = std::max(1, std::min(a.nchunks, 1024 / a.epr));
-    a.idbits = 32 - __builtin_clz((unsigned)num_experts);
-    int sthreads = 0, svec = 0;
-    dispatch_tile(&sthreads, &svec);
-    a.hchunks = (hidden / 8 + sthreads * svec - 1) / (sthreads * svec);
-    if ((int64_t)a.T * a.hchunks > 0x7FFFFFFFLL) return fail(MOE_ERR_UNSUPPORTED, "grid too large");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 sg((unsigned)((int64_t)a.T * a.hchunks)), sb(sthreads);
-    if (dispatch_path(a.pairs) == PATH_PLACE) {
-        hipLaunchKernelGGL(moe::dispatch_place, dim3((unsigned)((a.pairs + moe::kPlaceChunk - 1) / moe::kPlaceChunk)),
-                           dim3(moe::kPlace), 0, s, a);
-        launch_scatter<false>(svec, sg, sb, s, a);
-    } else {
-        hipLaunchKernelGGL(moe::dispatch_count, dim3(a.nchunks), dim3(64), 0, s, a);
-        hipLaunchKernelGGL(moe::dispatch_scan, dim3(ep_size), dim3(1024), 0, s, a);
-        launch_scatter<true>(svec, sg, sb, s, a);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return dispatch_launch(c, static_cast<int32_t *>(workspace), stream);
+}
+
+moe_status_t moe_dispatch_noalloc(const void *x, const int32_t *topk_ids, int64_t num_tokens, int32_t hidden,
+                                  int32_t top_k, int32_t num_experts, int32_t ep_size,
+                                  int64_t max_tokens_per_rank, void *payload, int32_t *src_info,
+                                  int32_t *recv_counts, void *stream) {
+    moe_call_args_t c = dispatch_call(x, topk_ids, num_tokens, hidden, top_k, num_experts, ep_size,
+                                      max_tokens_per_rank, payload, src_info, recv_counts);
+    moe_status_t st = moe_host::check_dispatch_own_scratch(c);
+    if (st != MOE_OK) return st;
+    if (num_tokens == 0) return ok();
+    // only the count + scan path keeps data in the workspace
+    const size_t need = dispatch_path(num_tokens * top_k) == PATH_PLACE
+                            ? 0 : moe_host::dispatch_workspace_bytes(num_tokens, top_k, num_experts);
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "this dispatch needs %zu bytes of scratch; moe_dispatch_noalloc holds at most %zu "
+                    "(use moe_dispatch with a workspace)", need, kScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != MOE_OK) return st;
+    return dispatch_launch(c, static_cast<int32_t *>(ws), stream);
 }
 
 moe_status_t moe_combine_describe_launch(int kind, int64_t num_tokens, int32_t hidden, int32_t top_k, char *buf,
