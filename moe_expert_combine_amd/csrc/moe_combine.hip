@@ -109,7 +109,17 @@ moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
         // The row reduction needs the whole token in one workgroup.
         if (!forced) {
             vec = 0;
+            // Rows of 6144 to 16384 elements: four vectors per lane (at
+            // H = 7168, 256 threads with the last 128 vectors masked). With
+            // slot tile 2 that measured 53.9 us against 54.3 us for 448 x 2 at
+            // T = 2048 (52.9 against 53.3 us with the MXFP8 copy) on MI355X:
+            // 4-wave workgroups, so more tokens are resident at once.
+            if (nvec >= 768 && (nvec + 3) / 4 <= 512) {
+                vec = 4;
+                threads = ((nvec + 3) / 4 + 63) / 64 * 64;
+            }
             for (int v : {1, 2, 4, 8}) {
+                if (vec) break;
                 const int t = ((nvec + v - 1) / v + 63) / 64 * 64;
                 if (t <= 512) {
                     vec = v;
@@ -138,10 +148,11 @@ moe_status_t make_plan(int kind, int64_t T, int32_t H, int32_t k, Plan *p) {
     while (p->kt * vec > 16) p->kt /= 2;
     // The RMSNorm epilogues run after a workgroup barrier; a smaller slot
     // tile frees registers for more resident workgroups, which hides that
-    // serial tail (measured on MI355X at T=2048, H=7168: slot tile 4 for
-    // RMSNorm, 2 when the normalised row is also quantised).
+    // serial tail (measured on MI355X at T=2048, H=7168: slot tile 2 with
+    // four vectors per lane; with two vectors per lane, slot tile 4 for
+    // RMSNorm and 2 when the normalised row is also quantised).
     if (!(forced && kt)) {
-        if (kind == moe::EPI_RMSNORM && p->kt > 4) p->kt = 4;
+        if (kind == moe::EPI_RMSNORM && p->kt > (vec >= 4 ? 2 : 4)) p->kt = vec >= 4 ? 2 : 4;
         if (kind == moe::EPI_RMSNORM_MXFP8 && p->kt > 2) p->kt = 2;
     }
     p->masked = (int64_t)p->chunks * threads * vec != nvec;

@@ -194,8 +194,12 @@ def test_describe_launch_shapes():
     d = mc.describe_launch(0, 100, 4096, 8)
     assert "chunks=4" in d and "masked=0" in d
     d = mc.describe_launch(1, 2048, 7168, 8)
-    assert "threads=448 vec_per_thread=2 chunks=1 blocks=2048 slot_tile=4" in d
-    assert "threads=448 vec_per_thread=2 chunks=1 blocks=2048 slot_tile=2" in mc.describe_launch(3, 2048, 7168, 8)
+    assert "threads=256 vec_per_thread=4 chunks=1 blocks=2048 slot_tile=2 masked=1" in d
+    assert "threads=256 vec_per_thread=4 chunks=1 blocks=2048 slot_tile=2 masked=1" in mc.describe_launch(3, 2048, 7168, 8)
+    # shorter and longer rows keep the narrowest shape that covers them
+    assert "threads=512 vec_per_thread=1 chunks=1 blocks=8 slot_tile=4 masked=0" in mc.describe_launch(1, 8, 4096, 8)
+    assert "threads=512 vec_per_thread=4" in mc.describe_launch(1, 8, 16384, 8)
+    assert "threads=384 vec_per_thread=8" in mc.describe_launch(1, 8, 24576, 8)
     with pytest.raises(mc.MoeCombineError):
         mc.describe_launch(3, 4, 48, 2)
     d = mc.describe_launch(2, 16384, 7168, 8)
@@ -224,9 +228,9 @@ def test_tile_override_env(monkeypatch):
     assert "threads=448 vec_per_thread=2 chunks=1 blocks=20 slot_tile=4" in mc.describe_launch(1, 20, 7168, 8)
     monkeypatch.setenv("MOE_COMBINE_TILE", "448x2x8")  # explicit slot tile wins
     assert "slot_tile=8" in mc.describe_launch(1, 20, 7168, 8)
-    monkeypatch.setenv("MOE_COMBINE_TILE", "448x2x3")  # bad slot tile -> ignored
-    assert "threads=448 vec_per_thread=2" in mc.describe_launch(1, 20, 7168, 8)
-    assert "slot_tile=4" in mc.describe_launch(1, 20, 7168, 8)
+    monkeypatch.setenv("MOE_COMBINE_TILE", "448x2x3")  # bad slot tile -> ignored (default shape)
+    assert "threads=256 vec_per_thread=4" in mc.describe_launch(1, 20, 7168, 8)
+    assert "slot_tile=2" in mc.describe_launch(1, 20, 7168, 8)
     monkeypatch.setenv("MOE_COMBINE_TILE", "100x3")   # invalid -> ignored
     assert "threads=64 vec_per_thread=2" in mc.describe_launch(0, 10, 7168, 8)
 
