@@ -315,7 +315,8 @@ def main():
     torch.cuda.synchronize()
     kms = np.array([a.elapsed_time(b) for a, b in ev])
     print(f"[bench] kernel mean {kernel_ms * 1e3:.1f} us over the timed region; per-launch "
-          f"p10 {np.percentile(kms, 10) * 1e3:.1f} p90 {np.percentile(kms, 90) * 1e3:.1f} us; "
+          f"median {np.median(kms) * 1e3:.1f} p10 {np.percentile(kms, 10) * 1e3:.1f} "
+          f"p90 {np.percentile(kms, 90) * 1e3:.1f} us; "
           f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
     if args.copy_probe:
@@ -378,6 +379,7 @@ def main():
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": algo_bytes,
                      "kernel_us_mean": kernel_ms * 1e3,
+                     "kernel_us_median_per_launch_events": float(np.median(kms) * 1e3),
                      "kernel_us_p10_p90_per_launch_events": [float(np.percentile(kms, 10) * 1e3),
                                                              float(np.percentile(kms, 90) * 1e3)]},
         "cpu_baseline": cpu,
