@@ -5,7 +5,8 @@
  * them. For token t, hidden index h, and slots j = 0..top_k-1 in ascending
  * order:
  *
- *   (rank, row) = src_info[t, j]              -- rank < 0: dropped slot
+ *   (rank, row) = src_info[t, j]              -- kept only if 0 <= rank < ep_size
+ *                                                and 0 <= row < max_tokens_per_rank
  *   acc  = +0.0f
  *   acc  = fmaf(w[t, j], payload[rank, row, h], acc)   for every kept slot
  *   acc += shared_out[t, h]                   -- only if shared_out != NULL
@@ -42,10 +43,11 @@
  *    output rows are in dispatch order.
  *  - src_info: [num_tokens, top_k, 2] int32 = (rank, row) per (token, slot).
  *    A slot with rank < 0 is dropped: it reads nothing, and its weight is
- *    ignored (the other weights are not renormalised). For a kept slot the
- *    caller guarantees 0 <= rank < ep_size and 0 <= row <
- *    max_tokens_per_rank. The library does not check slot ranges on the
- *    device; an out-of-range slot reads outside the payload.
+ *    ignored (the other weights are not renormalised). The pages only
+ *    require a kept slot to name a payload row; any slot outside the payload
+ *    (rank >= ep_size, row < 0 or row >= max_tokens_per_rank) is dropped the
+ *    same way. The kernels check both bounds before every row read, so no
+ *    slot map can make them read outside the payload.
  *  - router_weights: [num_tokens, top_k] fp32, or NULL for unit weights.
  *  - shared_out: [num_tokens, hidden] bf16, or NULL. It is added unweighted,
  *    after the routed sum.

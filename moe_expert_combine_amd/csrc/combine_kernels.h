@@ -11,6 +11,10 @@
 // a lane keeps KT * V 16-byte loads in flight; dropped slots (rank < 0) are
 // skipped with a uniform branch and read nothing.
 //
+// A slot reads its row only if 0 <= rank < ep and 0 <= row < rows per rank
+// (two scalar compares); any other slot, rank < 0 included, is dropped, so a
+// bad slot map cannot read outside the payload.
+//
 // Arithmetic (Struct_ep_combine_skip_a2a, execute: weighted sum of the
 // routed expert outputs; Parameter fused_shared_expert): acc starts at +0 and
 // takes one fp32 fused multiply-add per kept slot in ascending slot order,
@@ -45,6 +49,9 @@ struct KernelArgs {
     int32_t H;                 // hidden
     int32_t nvec;              // H / 8
     int32_t k;                 // top_k
+    int32_t ranks;             // ep: the payload's first dimension
+    int32_t rows;              // min(mtpr, 2^31 - 1): rows a slot may name
+    int64_t rank_elems;        // mtpr * H: elements per rank of the payload
     int32_t chunks;            // workgroups per token
     float eps;
     float wb;
@@ -380,8 +387,14 @@ __device__ __forceinline__ void gather_sum(const KernelArgs &a, int t, const int
         }
 #pragma unroll
         for (int jj = 0; jj < KT; ++jj) {
-            valid[jj] = r[jj] >= 0;
-            base[jj] = valid[jj] ? a.payload + ((int64_t)r[jj] * a.mtpr + row[jj]) * a.H : a.payload;
+            // rank < 0 marks a dropped slot; a slot outside the payload
+            // reads nothing either. Both bounds in one unsigned compare
+            // each, combined without a branch; the row offset is formed
+            // from the per-rank stride (fewer 64-bit scalar multiplies).
+            const unsigned ur = (unsigned)r[jj], uw = (unsigned)row[jj];
+            valid[jj] = (ur < (unsigned)a.ranks) & (uw < (unsigned)a.rows);
+            const int64_t off = (int64_t)ur * a.rank_elems + (int64_t)((uint64_t)uw * (unsigned)a.H);
+            base[jj] = a.payload + (valid[jj] ? off : 0);
         }
         u32x4 x[KT][V];
 #pragma unroll

@@ -203,8 +203,10 @@ moe_status_t launch(const Plan &p, const moe::KernelArgs &a, void *stream) {
     return ok();
 }
 
+// ranks, mtpr: the payload's first two dimensions (for the dense reduce, the
+// inputs and the tokens), which bound the slots the kernel reads.
 moe::KernelArgs base_args(const void *payload, const int32_t *src_info, const float *w, const void *shared,
-                          int32_t H, int32_t k, int64_t mtpr, const Plan &p) {
+                          int32_t H, int32_t k, int32_t ranks, int64_t mtpr, const Plan &p) {
     moe::KernelArgs a;
     memset(&a, 0, sizeof a);
     a.payload = static_cast<const uint16_t *>(payload);
@@ -215,6 +217,9 @@ moe::KernelArgs base_args(const void *payload, const int32_t *src_info, const fl
     a.H = H;
     a.nvec = H / 8;
     a.k = k;
+    a.ranks = ranks;
+    a.rows = (int32_t)std::min<int64_t>(mtpr, 0x7FFFFFFF);
+    a.rank_elems = mtpr * H;
     a.chunks = p.chunks;
     return a;
 }
@@ -367,7 +372,7 @@ moe_status_t moe_combine(const void *payload, const int32_t *src_info, const flo
     bool skip;
     moe_status_t st = prepare(c, moe::EPI_BF16, top_k, &p, &skip);
     if (st != MOE_OK || skip) return st;
-    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, ep_size, max_tokens_per_rank, p);
     a.out0 = out;
     return launch<moe::EPI_BF16>(p, a, stream);
 }
@@ -389,7 +394,7 @@ moe_status_t moe_combine_residual_rmsnorm(const void *payload, const int32_t *sr
     bool skip;
     moe_status_t st = prepare(c, moe::EPI_RMSNORM, top_k, &p, &skip);
     if (st != MOE_OK || skip) return st;
-    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, ep_size, max_tokens_per_rank, p);
     a.residual = static_cast<const uint16_t *>(residual_in);
     a.gamma = static_cast<const uint16_t *>(gamma);
     a.out0 = residual_out;
@@ -411,7 +416,7 @@ moe_status_t moe_combine_mxfp8(const void *payload, const int32_t *src_info, con
     bool skip;
     moe_status_t st = prepare(c, moe::EPI_MXFP8, top_k, &p, &skip);
     if (st != MOE_OK || skip) return st;
-    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, ep_size, max_tokens_per_rank, p);
     a.out0 = out_fp8;
     a.out1 = out_scales;
     return launch<moe::EPI_MXFP8>(p, a, stream);
@@ -429,7 +434,7 @@ moe_status_t moe_combine_mxfp4(const void *payload, const int32_t *src_info, con
     bool skip;
     moe_status_t st = prepare(c, moe::EPI_MXFP4, top_k, &p, &skip);
     if (st != MOE_OK || skip) return st;
-    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, ep_size, max_tokens_per_rank, p);
     a.out0 = out_fp4;
     a.out1 = out_scales;
     return launch<moe::EPI_MXFP4>(p, a, stream);
@@ -456,7 +461,7 @@ moe_status_t moe_combine_residual_rmsnorm_mxfp8(const void *payload, const int32
     bool skip;
     moe_status_t st = prepare(c, moe::EPI_RMSNORM_MXFP8, top_k, &p, &skip);
     if (st != MOE_OK || skip) return st;
-    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, max_tokens_per_rank, p);
+    moe::KernelArgs a = base_args(payload, src_info, router_weights, shared_out, hidden, top_k, ep_size, max_tokens_per_rank, p);
     a.residual = static_cast<const uint16_t *>(residual_in);
     a.gamma = static_cast<const uint16_t *>(gamma);
     a.out0 = residual_out;
@@ -476,7 +481,7 @@ moe_status_t moe_reduce_dense(const void *inputs, int32_t n_in, const float *sca
     bool skip;
     moe_status_t st = prepare(c, moe::EPI_BF16, n_in, &p, &skip);
     if (st != MOE_OK || skip) return st;
-    moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, num_tokens, p);
+    moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, n_in, num_tokens, p);
     a.out0 = out;
     return launch<moe::EPI_BF16>(p, a, stream);
 }
@@ -497,7 +502,7 @@ moe_status_t moe_reduce_dense_residual_rmsnorm(const void *inputs, int32_t n_in,
     bool skip;
     moe_status_t st = prepare(c, moe::EPI_RMSNORM, n_in, &p, &skip);
     if (st != MOE_OK || skip) return st;
-    moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, num_tokens, p);
+    moe::KernelArgs a = base_args(inputs, nullptr, scales, token_input, hidden, n_in, n_in, num_tokens, p);
     a.residual = static_cast<const uint16_t *>(residual_in);
     a.gamma = static_cast<const uint16_t *>(gamma);
     a.out0 = residual_out;

@@ -12,6 +12,7 @@ Acceptance, per output:
 Outputs are poisoned first, so every element the kernel should write is
 checked, and rows past num_tokens must keep the poison.
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -83,8 +84,8 @@ def check_mxfp8(codes, scales, rc, rs, what):
 
 # ----------------------------------------------------------------- runners
 
-def run_combine(inp, extra_rows=0):
-    d = to_dev(inp)
+def run_combine(inp, extra_rows=0, d=None):
+    d = d or to_dev(inp)
     out = poisoned16(inp.T, inp.H, extra_rows)
     mc.moe_combine(d["payload"], d["src_info"], d["weights"], d["shared"], out=out)
     torch.cuda.synchronize()
@@ -94,8 +95,8 @@ def run_combine(inp, extra_rows=0):
     return o[:inp.T]
 
 
-def run_rmsnorm(inp, wb, extra_rows=0, in_place=False):
-    d = to_dev(inp)
+def run_rmsnorm(inp, wb, extra_rows=0, in_place=False, d=None):
+    d = d or to_dev(inp)
     norm = poisoned16(inp.T, inp.H, extra_rows)
     if in_place:
         ro = torch.cat([d["residual"], poisoned16(0, inp.H, extra_rows)]) if extra_rows else d["residual"]
@@ -113,8 +114,8 @@ def run_rmsnorm(inp, wb, extra_rows=0, in_place=False):
     return a[:inp.T], b[:inp.T]
 
 
-def run_mxfp8(inp, extra_rows=0):
-    d = to_dev(inp)
+def run_mxfp8(inp, extra_rows=0, d=None):
+    d = d or to_dev(inp)
     T, H = inp.T, inp.H
     codes = torch.full((T + extra_rows, H), POISON8, dtype=torch.uint8, device=DEV)
     scales = torch.full((T + extra_rows, H // 32), POISON8, dtype=torch.uint8, device=DEV)
@@ -127,8 +128,8 @@ def run_mxfp8(inp, extra_rows=0):
     return c[:T], s[:T]
 
 
-def run_rmsnorm_mxfp8(inp, wb, extra_rows=0, want_norm=True):
-    d = to_dev(inp)
+def run_rmsnorm_mxfp8(inp, wb, extra_rows=0, want_norm=True, d=None):
+    d = d or to_dev(inp)
     T, H = inp.T, inp.H
     ro = poisoned16(T, H, extra_rows)
     no = poisoned16(T, H, extra_rows) if want_norm else None
@@ -148,18 +149,19 @@ def run_rmsnorm_mxfp8(inp, wb, extra_rows=0, want_norm=True):
     return a[:T], (b[:T] if want_norm else None), c[:T], sc[:T]
 
 
-def check_rmsnorm_mxfp8(inp, wb, extra_rows=0, want_norm=True, what=""):
-    ro, no, c, sc = run_rmsnorm_mxfp8(inp, wb, extra_rows, want_norm)
+def check_rmsnorm_mxfp8(inp, wb, extra_rows=0, want_norm=True, what="", ref=None, d=None):
+    ro, no, c, sc = run_rmsnorm_mxfp8(inp, wb, extra_rows, want_norm, d)
+    ref = inp if ref is None else ref
     rro, rno, rc, rs = oracle.combine_residual_rmsnorm_mxfp8(
-        inp.payload, inp.src_info, inp.weights, inp.shared, inp.residual, inp.gamma, inp.eps, wb)
+        ref.payload, ref.src_info, ref.weights, ref.shared, ref.residual, ref.gamma, ref.eps, wb)
     check_bf16(ro, rro, 1e-3, f"{what} residual_out (rmsnorm+mxfp8) wb={wb}")
     if want_norm:
         check_bf16(no, rno, 1e-3, f"{what} norm_out (rmsnorm+mxfp8) wb={wb}")
     check_mxfp8(c, sc, rc, rs, f"{what} mxfp8 of norm wb={wb}")
 
 
-def run_mxfp4(inp, extra_rows=0):
-    d = to_dev(inp)
+def run_mxfp4(inp, extra_rows=0, d=None):
+    d = d or to_dev(inp)
     T, H = inp.T, inp.H
     codes = torch.full((T + extra_rows, H // 2), POISON8, dtype=torch.uint8, device=DEV)
     scales = torch.full((T + extra_rows, H // 32), POISON8, dtype=torch.uint8, device=DEV)
@@ -195,24 +197,27 @@ def oracle_all(inp, kind, wb=0.0):
     return oracle.combine_mxfp8(inp.payload, inp.src_info, inp.weights, inp.shared)
 
 
-def check_all_kinds(inp, wbs=(0.0, 1.0), extra_rows=3, what=""):
-    check_bf16(run_combine(inp, extra_rows), oracle_all(inp, "bf16"), 1e-3, f"{what} combine")
+def check_all_kinds(inp, wbs=(0.0, 1.0), extra_rows=3, what="", ref=None, d=None):
+    """Every output kind of the HIP path on inp against the oracle on ref
+    (default: the same inputs). d: device tensors for inp, if prebuilt."""
+    ref = inp if ref is None else ref
+    check_bf16(run_combine(inp, extra_rows, d), oracle_all(ref, "bf16"), 1e-3, f"{what} combine")
     if inp.residual is not None:
         for wb in wbs:
-            ro, no = run_rmsnorm(inp, wb, extra_rows)
-            rro, rno = oracle_all(inp, "rmsnorm", wb)
+            ro, no = run_rmsnorm(inp, wb, extra_rows, d=d)
+            rro, rno = oracle_all(ref, "rmsnorm", wb)
             check_bf16(ro, rro, 1e-3, f"{what} residual_out wb={wb}")
             check_bf16(no, rno, 1e-3, f"{what} norm_out wb={wb}")
     if inp.H % 32 == 0:
-        c, s = run_mxfp8(inp, extra_rows)
-        rc, rs = oracle_all(inp, "mxfp8")
+        c, s = run_mxfp8(inp, extra_rows, d)
+        rc, rs = oracle_all(ref, "mxfp8")
         check_mxfp8(c, s, rc, rs, f"{what} mxfp8")
-        c4, s4 = run_mxfp4(inp, extra_rows)
-        rc4, rs4 = oracle.combine_mxfp4(inp.payload, inp.src_info, inp.weights, inp.shared)
+        c4, s4 = run_mxfp4(inp, extra_rows, d)
+        rc4, rs4 = oracle.combine_mxfp4(ref.payload, ref.src_info, ref.weights, ref.shared)
         check_mxfp4(c4, s4, rc4, rs4, f"{what} mxfp4")
         if inp.residual is not None:
             for i, wb in enumerate(wbs):
-                check_rmsnorm_mxfp8(inp, wb, extra_rows, want_norm=(i == 0), what=what)
+                check_rmsnorm_mxfp8(inp, wb, extra_rows, want_norm=(i == 0), what=what, ref=ref, d=d)
 
 
 def with_norm_inputs(c):
@@ -511,6 +516,61 @@ def test_all_slots_dropped_without_shared_gives_plus_zero():
     assert (run_combine(inp) == 0).all()
     c, s = run_mxfp8(inp)
     assert (c == 0).all() and (s == 0).all()
+
+
+# ------------------------------------------------ slots outside the payload
+
+def _padded_dev(inp, pad):
+    """Device tensors for inp whose payload sits between `pad` ranks of NaN
+    rows on each side, in one allocation. A slot outside the payload that the
+    kernel failed to drop would read those rows (NaN in the output) or another
+    real row (a wrong sum), never memory outside the allocation."""
+    d = to_dev(inp)
+    ep, mtpr, H = inp.payload.shape
+    host = np.full((ep + 2 * pad, mtpr, H), 0x7FC0, np.uint16)
+    host[pad:pad + ep] = inp.payload
+    d["payload_alloc"] = dev16(host)
+    d["payload"] = d["payload_alloc"][pad:pad + ep]
+    return d
+
+
+def _with_slots(inp, pairs, frac, seed):
+    """(inputs whose slot map names the (rank, row) pairs on a fraction of the
+    kept slots, the same inputs with exactly those slots dropped)."""
+    rng = np.random.default_rng(seed)
+    bad, clean = inp.src_info.copy(), inp.src_info.copy()
+    kept = np.argwhere(inp.src_info[..., 0] >= 0)
+    pick = kept[rng.random(len(kept)) < frac]
+    assert len(pick) >= len(pairs)
+    for n, (t, j) in enumerate(pick):
+        bad[t, j] = pairs[n % len(pairs)]
+        clean[t, j] = (-1, -1)
+    return dataclasses.replace(inp, src_info=bad), dataclasses.replace(inp, src_info=clean)
+
+
+def test_slots_just_outside_the_payload_are_dropped():
+    """A slot whose rank is outside [0, ep_size) or whose row is outside
+    [0, max_tokens_per_rank) reads nothing and counts as dropped, on every
+    output kind. Here the bad pairs stay within four ranks of the payload, and
+    the payload is padded by four NaN ranks on each side."""
+    inp = gen.make_inputs(with_norm_inputs(dict(T=41, H=1056, E=32, ep=4, k=8, shared_sd=0.5)), seed=11)
+    ep, m = inp.ep, inp.mtpr
+    pairs = [(ep, 0), (ep + 1, m - 1), (ep + 3, 7), (0, m), (ep - 1, m + 17), (1, 2 * m + 1),
+             (0, -1), (2, -1), (ep - 1, -m), (3, -3 * m), (-5, 3)]
+    for r, w in pairs:   # where an unchecked read would land, in rows of the padded allocation
+        assert r < 0 or -4 * m <= r * m + w < (ep + 4) * m
+    bad, clean = _with_slots(inp, pairs, 0.3, seed=11)
+    check_all_kinds(bad, ref=clean, d=_padded_dev(bad, pad=4), what="slots just outside the payload")
+
+
+def test_slots_far_outside_the_payload_are_dropped():
+    """Extreme ranks and rows (2^30, the int32 limits) are dropped too."""
+    inp = gen.make_inputs(with_norm_inputs(dict(T=29, H=2048, E=64, ep=8, k=6, shared_sd=0.5)), seed=12)
+    i32max, i32min = 2**31 - 1, -2**31
+    pairs = [(1 << 30, 0), (i32max, i32max), (0, i32max), (inp.ep - 1, i32min), (3, 1 << 30),
+             (i32max, -1), (i32min, 0)]
+    bad, clean = _with_slots(inp, pairs, 0.3, seed=12)
+    check_all_kinds(bad, ref=clean, what="slots far outside the payload")
 
 
 def test_zero_tokens_leaves_outputs_untouched():
