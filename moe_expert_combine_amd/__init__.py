@@ -9,7 +9,8 @@ every call raises.
 
 Layouts (see the header for the full contract):
   payload        bf16  [ep_size, max_tokens_per_rank, hidden]
-  src_info       int32 [num_tokens, top_k, 2]   (rank, row); rank < 0 dropped
+  src_info       int32 [num_tokens, top_k, 2]   (rank, row); rank < 0, or a slot outside
+                                                the payload, is dropped
   router_weights fp32  [num_tokens, top_k]      or None (unit weights)
   shared_out     bf16  [num_tokens, hidden]     or None
 Outputs may be passed in with at least num_tokens rows; only the first

@@ -8,8 +8,8 @@
 //
 // Per token the slot map and weights are wave-uniform (scalar loads). For
 // each group of KT slots all row loads are issued before any arithmetic, so
-// a lane keeps KT * V 16-byte loads in flight; dropped slots (rank < 0) are
-// skipped with a uniform branch and read nothing.
+// a lane keeps KT * V 16-byte loads in flight; dropped slots are skipped
+// with a uniform branch and read nothing.
 //
 // A slot reads its row only if 0 <= rank < ep and 0 <= row < rows per rank
 // (two scalar compares); any other slot, rank < 0 included, is dropped, so a
