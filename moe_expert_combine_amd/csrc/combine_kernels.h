@@ -50,7 +50,7 @@ struct KernelArgs {
     int32_t nvec;              // H / 8
     int32_t k;                 // top_k
     int32_t ranks;             // ep: the payload's first dimension
-    int32_t rows;              // min(mtpr, 2^31 - 1): rows a slot may name
+    uint32_t rows;             // min(mtpr, 2^31): a slot's row must be below it (unsigned)
     int64_t rank_elems;        // mtpr * H: elements per rank of the payload
     int32_t chunks;            // workgroups per token
     float eps;
@@ -392,7 +392,7 @@ __device__ __forceinline__ void gather_sum(const KernelArgs &a, int t, const int
             // each, combined without a branch; the row offset is formed
             // from the per-rank stride (fewer 64-bit scalar multiplies).
             const unsigned ur = (unsigned)r[jj], uw = (unsigned)row[jj];
-            valid[jj] = (ur < (unsigned)a.ranks) & (uw < (unsigned)a.rows);
+            valid[jj] = (ur < (unsigned)a.ranks) & (uw < a.rows);
             const int64_t off = (int64_t)ur * a.rank_elems + (int64_t)((uint64_t)uw * (unsigned)a.H);
             base[jj] = a.payload + (valid[jj] ? off : 0);
         }

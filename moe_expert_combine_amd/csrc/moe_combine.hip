@@ -218,7 +218,8 @@ moe::KernelArgs base_args(const void *payload, const int32_t *src_info, const fl
     a.nvec = H / 8;
     a.k = k;
     a.ranks = ranks;
-    a.rows = (int32_t)std::min<int64_t>(mtpr, 0x7FFFFFFF);
+    // every int32 row >= 0 is below 2^31, so this bound is exact for any mtpr
+    a.rows = (uint32_t)std::min<int64_t>(mtpr, int64_t(1) << 31);
     a.rank_elems = mtpr * H;
     a.chunks = p.chunks;
     return a;
