@@ -9,8 +9,9 @@ roofline. ``value`` is tokens per second of wall-clock time over the
 timed region.
 
 Default workload: T=4096, hidden=7168, top_k=8, 256 experts over 8 simulated
-ranks, bf16 output. Other workloads: --workload skewed | rmsnorm | mxfp8 |
-tiny.
+ranks, bf16 output. Other workloads (--workload): skewed, rmsnorm,
+rmsnorm_mxfp8, mxfp8, mxfp4, dense8 (the local reduce), dispatch (placement
++ row scatter, both kernels per step) and tiny.
 
 The CPU baseline is the oracle (C, OpenMP), timed on the host cores on the
 same host arrays: the median of three batches of whole-workload runs (about
